@@ -1,0 +1,11 @@
+"""MI355X (gfx950) ring-attention per-device hot path.
+
+The computation lives in the HIP library ``libra.so`` (C ABI: include/ra.h);
+this package only loads it and marshals torch tensors into its calls.
+"""
+from .api import (  # noqa: F401
+    LAYOUTS, KernelTimes, block_attn_bwd, block_attn_fwd, bwd_preprocess, cast_f32_to_bf16,
+    kernel_timing, layout_positions, layout_posmap, lse_merge, posmap, ring_bwd, ring_fwd,
+    ring_workspace_bytes,
+)
+from ._lib import RAError, lib  # noqa: F401

@@ -1,0 +1,286 @@
+"""Thin PyTorch-facing binding of the ring-attention C ABI.
+
+Only argument marshalling happens here: torch supplies device memory and the
+current HIP stream; every step of the computation runs in libra.so's kernels.
+Tensors are token-major [batch, tokens, heads, head_dim] with a contiguous
+last axis; K/V rings are [world, batch, tokens, heads, head_dim].
+"""
+from __future__ import annotations
+
+import ctypes as C
+from contextlib import contextmanager
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import check, lib, ra_posmap, ra_problem, ra_seg, ra_tensor
+
+LAYOUTS = tuple(_lib.LAYOUT_IDS)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_id(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    if dt == torch.float32:
+        return _lib.DTYPE_F32
+    raise TypeError(f"unsupported dtype {dt} (bf16 or fp32)")
+
+
+def _layout_id(layout: str) -> int:
+    try:
+        return _lib.LAYOUT_IDS[layout]
+    except KeyError:
+        raise ValueError(f"unknown layout {layout!r}; expected one of {LAYOUTS}") from None
+
+
+def _t4(x) -> ra_tensor:
+    """ra_tensor for a [b, tokens, heads, dim] tensor (None -> empty)."""
+    if x is None:
+        return ra_tensor(None, 0, 0, 0)
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("expected a [batch, tokens, heads, head_dim] tensor with contiguous head_dim")
+    if not x.is_cuda:
+        raise ValueError("tensors must be device (HIP) tensors")
+    return ra_tensor(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
+
+
+def _t5(x) -> Tuple[ra_tensor, int]:
+    """ra_tensor of block 0 of a [world, b, tokens, heads, dim] ring, and its rank stride."""
+    if x.dim() != 5 or x.stride(4) != 1:
+        raise ValueError("expected a [world, batch, tokens, heads, head_dim] ring with contiguous head_dim")
+    if not x.is_cuda:
+        raise ValueError("tensors must be device (HIP) tensors")
+    return ra_tensor(x.data_ptr(), x.stride(1), x.stride(2), x.stride(3)), x.stride(0)
+
+
+def _stream() -> int:
+    return _torch().cuda.current_stream().cuda_stream
+
+
+class _Cu:
+    """Keeps the device and host copies of cu_seqlens alive for a call."""
+
+    def __init__(self, cu_seqlens, device):
+        torch = _torch()
+        self.dev = None
+        self.host = None
+        self.n = 0
+        if cu_seqlens is None:
+            return
+        if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+            self.dev = cu_seqlens.to(torch.int32).contiguous()
+            self.host = None
+        else:
+            self.host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+            self.dev = torch.from_numpy(self.host).to(device)
+        self.n = int(self.dev.numel()) - 1
+
+    def fill(self, p: ra_problem):
+        if self.dev is None:
+            p.cu_seqlens = None
+            p.cu_seqlens_host = None
+            p.num_seqs = 0
+        else:
+            p.cu_seqlens = self.dev.data_ptr()
+            p.cu_seqlens_host = self.host.ctypes.data if self.host is not None else None
+            p.num_seqs = self.n
+
+
+def _problem(x, heads: int, head_dim: int, seq_len: int, causal: bool, scale: Optional[float], cu: _Cu) -> ra_problem:
+    p = ra_problem()
+    p.batch = x.shape[0] if x.dim() == 4 else x.shape[1]
+    p.heads = heads
+    p.head_dim = head_dim
+    p.dtype = _dtype_id(x.dtype)
+    p.softmax_scale = float(scale) if scale is not None else 0.0
+    p.causal = 1 if causal else 0
+    p.seq_len = int(seq_len)
+    cu.fill(p)
+    return p
+
+
+# ---- layouts -------------------------------------------------------------------------------
+
+def layout_positions(layout: str, seq_len: int, world: int, rank: int) -> np.ndarray:
+    """Global positions of ``rank``'s local tokens (as the library lays them out)."""
+    out = np.empty(seq_len // max(world, 1), dtype=np.int64)
+    check(lib().ra_layout_positions(_layout_id(layout), seq_len, world, rank,
+                                    out.ctypes.data_as(C.POINTER(C.c_int64))))
+    return out
+
+
+def layout_posmap(layout: str, seq_len: int, world: int, rank: int) -> ra_posmap:
+    m = ra_posmap()
+    check(lib().ra_layout_posmap(_layout_id(layout), seq_len, world, rank, C.byref(m)))
+    return m
+
+
+def posmap(segments: Sequence[Tuple[int, int, int]]) -> ra_posmap:
+    """Posmap from up to two (begin, stride, len) runs in local order."""
+    if not 1 <= len(segments) <= 2:
+        raise ValueError("one or two segments")
+    m = ra_posmap()
+    m.nseg = len(segments)
+    for i, (b, s, n) in enumerate(segments):
+        m.seg[i] = ra_seg(int(b), int(s), int(n))
+    return m
+
+
+# ---- block level ---------------------------------------------------------------------------
+
+def block_attn_fwd(q, k, v, qmap: ra_posmap, kmap: ra_posmap, *, seq_len: int, causal: bool = False,
+                   cu_seqlens=None, scale: Optional[float] = None, out_b=None, lse_b=None):
+    """One block step: returns (out_b fp32 [b, lq, h, d], lse_b fp32 [b, h, lq])."""
+    torch = _torch()
+    b, lq, h, d = q.shape
+    lk = k.shape[1]
+    if out_b is None:
+        out_b = torch.empty((b, lq, h, d), device=q.device, dtype=torch.float32)
+    if lse_b is None:
+        lse_b = torch.empty((b, h, lq), device=q.device, dtype=torch.float32)
+    cu = _Cu(cu_seqlens, q.device)
+    p = _problem(q, h, d, seq_len, causal, scale, cu)
+    check(lib().ra_block_attn_fwd(C.byref(p), _t4(q), lq, qmap, _t4(k), _t4(v), lk, kmap, _t4(out_b),
+                                  lse_b.data_ptr(), _stream()))
+    return out_b, lse_b
+
+
+def lse_merge(out, lse, out_b, lse_b) -> None:
+    """In place: (out, lse) <- merge((out, lse), (out_b, lse_b)); all fp32."""
+    b, lq, h, d = out.shape
+    p = ra_problem()
+    p.batch, p.heads, p.head_dim, p.dtype = b, h, d, _lib.DTYPE_F32
+    check(lib().ra_lse_merge(C.byref(p), lq, _t4(out), lse.data_ptr(), _t4(out_b), lse_b.data_ptr(), _stream()))
+
+
+def bwd_preprocess(out, dout):
+    """delta = rowsum(dout * out) as fp32 [b, h, lq]."""
+    torch = _torch()
+    b, lq, h, d = out.shape
+    delta = torch.empty((b, h, lq), device=out.device, dtype=torch.float32)
+    p = ra_problem()
+    p.batch, p.heads, p.head_dim, p.dtype = b, h, d, _dtype_id(dout.dtype)
+    check(lib().ra_bwd_preprocess(C.byref(p), lq, _t4(out), _t4(dout), delta.data_ptr(), _stream()))
+    return delta
+
+
+def block_attn_bwd(q, k, v, dout, lse, delta, qmap: ra_posmap, kmap: ra_posmap, dq_acc, dk_acc, dv_acc, *,
+                   seq_len: int, causal: bool = False, cu_seqlens=None, scale: Optional[float] = None) -> None:
+    """Accumulate one block step's gradients into dq_acc/dk_acc/dv_acc (fp32)."""
+    b, lq, h, d = q.shape
+    lk = k.shape[1]
+    cu = _Cu(cu_seqlens, q.device)
+    p = _problem(q, h, d, seq_len, causal, scale, cu)
+    check(lib().ra_block_attn_bwd(C.byref(p), _t4(q), lq, qmap, _t4(k), _t4(v), lk, kmap, _t4(dout),
+                                  lse.data_ptr(), delta.data_ptr(), _t4(dq_acc), _t4(dk_acc), _t4(dv_acc),
+                                  _stream()))
+
+
+# ---- virtual ring --------------------------------------------------------------------------
+
+def ring_fwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, *, causal: bool = True,
+             cu_seqlens=None, scale: Optional[float] = None, out=None, lse=None, want_lowp: bool = False,
+             out_lowp=None):
+    """Rank ``rank``'s share of the virtual ring.  Returns (out fp32, lse fp32, out_lowp or None)."""
+    torch = _torch()
+    b, L, h, d = q_local.shape
+    S = L * world
+    if out is None:
+        out = torch.empty((b, L, h, d), device=q_local.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty((b, h, L), device=q_local.device, dtype=torch.float32)
+    if want_lowp and out_lowp is None:
+        out_lowp = torch.empty((b, L, h, d), device=q_local.device, dtype=q_local.dtype)
+    cu = _Cu(cu_seqlens, q_local.device)
+    p = _problem(q_local, h, d, S, causal, scale, cu)
+    kt, srank = _t5(k_ring)
+    vt, srank_v = _t5(v_ring)
+    if srank != srank_v:
+        raise ValueError("k_ring and v_ring must share the rank stride")
+    check(lib().ra_ring_fwd(C.byref(p), _layout_id(layout), world, rank, _t4(q_local), kt, vt, srank,
+                            _t4(out), lse.data_ptr(), _t4(out_lowp), _stream()))
+    return out, lse, out_lowp
+
+
+def ring_workspace_bytes(layout: str, world: int, q_local, causal: bool = True) -> int:
+    b, L, h, d = q_local.shape
+    p = _problem(q_local, h, d, L * world, causal, None, _Cu(None, None))
+    return int(lib().ra_ring_workspace_bytes(C.byref(p), _layout_id(layout), world))
+
+
+def ring_bwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, out, lse, dout, *,
+             causal: bool = True, cu_seqlens=None, scale: Optional[float] = None,
+             dq=None, dk_ring=None, dv_ring=None, workspace=None):
+    """Backward of rank ``rank``'s share.  dq is overwritten; dk_ring/dv_ring (fp32) are accumulated
+    (allocated zeroed when not given).  Returns (dq, dk_ring, dv_ring)."""
+    torch = _torch()
+    b, L, h, d = q_local.shape
+    S = L * world
+    dev = q_local.device
+    if dq is None:
+        dq = torch.empty((b, L, h, d), device=dev, dtype=torch.float32)
+    if dk_ring is None:
+        dk_ring = torch.zeros((world, b, L, h, d), device=dev, dtype=torch.float32)
+    if dv_ring is None:
+        dv_ring = torch.zeros((world, b, L, h, d), device=dev, dtype=torch.float32)
+    cu = _Cu(cu_seqlens, dev)
+    p = _problem(q_local, h, d, S, causal, scale, cu)
+    need = int(lib().ra_ring_workspace_bytes(C.byref(p), _layout_id(layout), world))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=dev, dtype=torch.uint8)
+    kt, srank = _t5(k_ring)
+    vt, _ = _t5(v_ring)
+    dkt, sgrad = _t5(dk_ring)
+    dvt, sgrad_v = _t5(dv_ring)
+    if sgrad != sgrad_v:
+        raise ValueError("dk_ring and dv_ring must share the rank stride")
+    check(lib().ra_ring_bwd(C.byref(p), _layout_id(layout), world, rank, _t4(q_local), kt, vt, srank,
+                            _t4(out), lse.data_ptr(), _t4(dout), _t4(dq), dkt, dvt, sgrad,
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return dq, dk_ring, dv_ring
+
+
+def cast_f32_to_bf16(x, out=None):
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("expected a contiguous fp32 tensor")
+    if out is None:
+        out = torch.empty(x.shape, device=x.device, dtype=torch.bfloat16)
+    check(lib().ra_cast_f32_to_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream()))
+    return out
+
+
+# ---- kernel timing -------------------------------------------------------------------------
+
+class KernelTimes:
+    def __init__(self):
+        self.launches: List[Tuple[str, int, float]] = []
+
+    def by_kernel(self):
+        agg = {}
+        for name, _, ms in self.launches:
+            n, t = agg.get(name, (0, 0.0))
+            agg[name] = (n + 1, t + ms)
+        return agg
+
+
+@contextmanager
+def kernel_timing(capacity: int = 4096):
+    """Record HIP events around every library kernel launched inside the block."""
+    res = KernelTimes()
+    check(lib().ra_timing_begin(capacity))
+    try:
+        yield res
+    finally:
+        buf = (_lib.ra_launch_time * capacity)()
+        n = C.c_int32(0)
+        check(lib().ra_timing_end(buf, capacity, C.byref(n)))
+        for i in range(n.value):
+            res.launches.append((lib().ra_kernel_name(buf[i].kernel_id).decode(), buf[i].step, buf[i].ms))

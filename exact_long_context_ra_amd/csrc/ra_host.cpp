@@ -1,0 +1,649 @@
+// Host side of the C ABI declared in include/ra.h: argument validation, the
+// token-to-device layouts, the virtual-ring step planner and kernel timing.
+//
+// Layouts ("Ring Flash Attention" README function list; guijiagi.com Ring
+// Attention article, sections on the detailed flow and on striped ring
+// attention; Striped Attention abstract on briefgpt.xyz):
+//   contiguous  rank r owns positions [r*L, (r+1)*L)                 L = S/N
+//   zigzag      rank r owns chunks r and 2N-1-r of size C = S/(2N), in that order
+//   stripe      rank r owns positions r, r+N, r+2N, ...
+// Ring schedule (same article, detailed flow): at step s the rank works on the
+// block of rank (r - s) mod N.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/ra.h"
+#include "ra_internal.h"
+
+using namespace ra;
+
+namespace {
+
+thread_local char g_err[1024] = "";
+
+ra_status fail(ra_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define RA_CHECK(cond, status, ...) \
+  do {                              \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define RA_HIP(expr)                                                                               \
+  do {                                                                                             \
+    hipError_t e_ = (expr);                                                                        \
+    if (e_ != hipSuccess) return fail(RA_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int64_t kMaxPos = 0x7fffffffLL;
+
+// ---- timing -------------------------------------------------------------------------------
+
+struct Timing {
+  bool on = false;
+  int cap = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev0, ev1;
+  std::vector<int32_t> kid, step;
+};
+thread_local Timing g_timing;
+
+template <class F>
+hipError_t timed(KernelId id, int step, hipStream_t s, F&& f) {
+  Timing& t = g_timing;
+  if (!t.on || t.n >= t.cap) return f();
+  const int i = t.n;
+  hipError_t e = hipEventRecord(t.ev0[i], s);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.ev1[i], s);
+  if (e != hipSuccess) return e;
+  t.kid[i] = id;
+  t.step[i] = step;
+  t.n = i + 1;
+  return hipSuccess;
+}
+
+// ---- validation ---------------------------------------------------------------------------
+
+ra_status check_problem(const ra_problem* p) {
+  RA_CHECK(p != nullptr, RA_ERR_INVALID_ARG, "problem is NULL");
+  RA_CHECK(p->batch >= 1 && p->heads >= 1, RA_ERR_INVALID_ARG, "batch (%d) and heads (%d) must be >= 1", p->batch,
+           p->heads);
+  RA_CHECK(p->dtype == RA_DTYPE_F32 || p->dtype == RA_DTYPE_BF16, RA_ERR_INVALID_ARG, "unknown dtype %d",
+           (int)p->dtype);
+  RA_CHECK(p->head_dim == 64 || p->head_dim == 128, RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)",
+           p->head_dim);
+  RA_CHECK(p->seq_len >= 0 && p->seq_len <= kMaxPos, RA_ERR_INVALID_ARG, "seq_len %lld out of range",
+           (long long)p->seq_len);
+  RA_CHECK(isfinite(p->softmax_scale), RA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  RA_CHECK(p->num_seqs >= 0, RA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (p->num_seqs > 0) {
+    RA_CHECK(p->cu_seqlens != nullptr, RA_ERR_INVALID_ARG, "num_seqs > 0 but cu_seqlens is NULL");
+    RA_CHECK(p->batch == 1, RA_ERR_INVALID_ARG, "cu_seqlens requires batch == 1 (got %d)", p->batch);
+    if (p->cu_seqlens_host) {
+      const int32_t* cu = p->cu_seqlens_host;
+      RA_CHECK(cu[0] == 0, RA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+      for (int i = 0; i < p->num_seqs; ++i)
+        RA_CHECK(cu[i + 1] >= cu[i], RA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (index %d)", i + 1);
+      RA_CHECK(cu[p->num_seqs] == p->seq_len, RA_ERR_INVALID_ARG, "cu_seqlens[num_seqs]=%d != seq_len=%lld",
+               cu[p->num_seqs], (long long)p->seq_len);
+    }
+  } else {
+    RA_CHECK(p->cu_seqlens == nullptr, RA_ERR_INVALID_ARG, "cu_seqlens given but num_seqs == 0");
+  }
+  return RA_OK;
+}
+
+size_t elem_size(ra_dtype d) { return d == RA_DTYPE_BF16 ? 2 : 4; }
+
+ra_status check_tensor(const char* name, const ra_tensor& t, size_t esz, int64_t rows, bool need) {
+  if (!need) return RA_OK;
+  RA_CHECK(t.ptr != nullptr, RA_ERR_INVALID_ARG, "%s: NULL pointer", name);
+  RA_CHECK(((uintptr_t)t.ptr & 15) == 0, RA_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", name);
+  RA_CHECK(t.stride_b >= 0 && t.stride_t >= 0 && t.stride_h >= 0, RA_ERR_INVALID_ARG, "%s: negative stride", name);
+  const int64_t b16 = 16 / (int64_t)esz;  // elements per 16 bytes
+  RA_CHECK(t.stride_b % b16 == 0 && t.stride_t % b16 == 0 && t.stride_h % b16 == 0, RA_ERR_INVALID_ARG,
+           "%s: strides must keep rows 16-byte aligned", name);
+  (void)rows;
+  return RA_OK;
+}
+
+ra_status check_ptr(const char* name, const void* p) {
+  RA_CHECK(p != nullptr, RA_ERR_INVALID_ARG, "%s: NULL pointer", name);
+  RA_CHECK(((uintptr_t)p & 3) == 0, RA_ERR_INVALID_ARG, "%s: pointer not 4-byte aligned", name);
+  return RA_OK;
+}
+
+int64_t pos_at(const ra_posmap& m, int64_t a) {
+  if (a < m.seg[0].len) return m.seg[0].begin + a * m.seg[0].stride;
+  return m.seg[1].begin + (a - m.seg[0].len) * m.seg[1].stride;
+}
+
+ra_status check_posmap(const char* name, const ra_posmap& m, int64_t len, int64_t seq_len) {
+  RA_CHECK(m.nseg == 1 || m.nseg == 2, RA_ERR_INVALID_ARG, "%s: nseg must be 1 or 2 (got %d)", name, m.nseg);
+  int64_t total = 0;
+  int64_t prev_last = -1;
+  for (int i = 0; i < m.nseg; ++i) {
+    const ra_seg& s = m.seg[i];
+    RA_CHECK(s.len >= 0 && s.stride >= 1 && s.begin >= 0, RA_ERR_INVALID_ARG,
+             "%s: segment %d needs len >= 0, stride >= 1, begin >= 0", name, i);
+    if (s.len > 0) {
+      const int64_t last = s.begin + (s.len - 1) * s.stride;
+      RA_CHECK(last < seq_len && last <= kMaxPos, RA_ERR_INVALID_ARG, "%s: segment %d exceeds seq_len", name, i);
+      RA_CHECK(s.begin > prev_last, RA_ERR_INVALID_ARG, "%s: positions must be strictly increasing", name);
+      prev_last = last;
+    }
+    total += s.len;
+  }
+  RA_CHECK(total == len, RA_ERR_INVALID_ARG, "%s: segment lengths sum to %lld, expected %lld", name,
+           (long long)total, (long long)len);
+  return RA_OK;
+}
+
+DMap to_dmap(const ra_posmap& m) {
+  DMap d{};
+  d.nseg = m.nseg;
+  d.s0 = DSeg{(int32_t)m.seg[0].begin, (int32_t)m.seg[0].stride, (int32_t)m.seg[0].len};
+  if (m.nseg == 2)
+    d.s1 = DSeg{(int32_t)m.seg[1].begin, (int32_t)m.seg[1].stride, (int32_t)m.seg[1].len};
+  else
+    d.s1 = DSeg{0, 1, 0};
+  d.total = d.s0.len + d.s1.len;
+  return d;
+}
+
+MaskSpec mask_of(const ra_problem* p) {
+  MaskSpec m{};
+  m.causal = p->causal ? 1 : 0;
+  m.nseq = p->num_seqs;
+  m.cu = p->cu_seqlens;
+  return m;
+}
+
+float scale_of(const ra_problem* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
+}
+
+Tensor4 rd(const ra_tensor& t) { return Tensor4{t.ptr, t.stride_b, t.stride_t, t.stride_h}; }
+Tensor4W wr(const ra_tensor& t) { return Tensor4W{t.ptr, t.stride_b, t.stride_t, t.stride_h}; }
+Tensor4 offset_rd(const ra_tensor& t, int64_t elems, size_t esz) {
+  return Tensor4{(const char*)t.ptr + elems * (int64_t)esz, t.stride_b, t.stride_t, t.stride_h};
+}
+Tensor4W offset_wr(const ra_tensor& t, int64_t elems, size_t esz) {
+  return Tensor4W{(char*)t.ptr + elems * (int64_t)esz, t.stride_b, t.stride_t, t.stride_h};
+}
+
+// ---- layouts ------------------------------------------------------------------------------
+
+ra_status make_posmap(ra_layout layout, int64_t S, int32_t N, int32_t r, ra_posmap* out) {
+  RA_CHECK(N >= 1, RA_ERR_INVALID_ARG, "world must be >= 1");
+  RA_CHECK(r >= 0 && r < N, RA_ERR_INVALID_ARG, "rank %d out of range [0, %d)", r, N);
+  RA_CHECK(S >= 0 && S <= kMaxPos, RA_ERR_INVALID_ARG, "seq_len out of range");
+  ra_posmap m{};
+  switch (layout) {
+    case RA_LAYOUT_CONTIGUOUS: {
+      RA_CHECK(S % N == 0, RA_ERR_INVALID_ARG, "contiguous: seq_len %lld not divisible by world %d", (long long)S, N);
+      const int64_t L = S / N;
+      m.nseg = 1;
+      m.seg[0] = ra_seg{r * L, 1, L};
+      break;
+    }
+    case RA_LAYOUT_ZIGZAG: {
+      RA_CHECK(S % (2 * (int64_t)N) == 0, RA_ERR_INVALID_ARG, "zigzag: seq_len %lld not divisible by 2*world",
+               (long long)S);
+      const int64_t C = S / (2 * (int64_t)N);
+      m.nseg = 2;
+      m.seg[0] = ra_seg{r * C, 1, C};
+      m.seg[1] = ra_seg{(2 * (int64_t)N - 1 - r) * C, 1, C};
+      break;
+    }
+    case RA_LAYOUT_STRIPE: {
+      RA_CHECK(S % N == 0, RA_ERR_INVALID_ARG, "stripe: seq_len %lld not divisible by world %d", (long long)S, N);
+      m.nseg = 1;
+      m.seg[0] = ra_seg{r, N, S / N};
+      break;
+    }
+    default:
+      return fail(RA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
+  }
+  *out = m;
+  return RA_OK;
+}
+
+// First local index with position >= P (len if none); last with position <= P (-1 if none).
+int64_t h_first_ge(const ra_posmap& m, int64_t P) {
+  int64_t off = 0;
+  for (int i = 0; i < m.nseg; ++i) {
+    const ra_seg& s = m.seg[i];
+    if (s.len > 0) {
+      const int64_t last = s.begin + (s.len - 1) * s.stride;
+      if (last >= P) return off + (P <= s.begin ? 0 : (P - s.begin + s.stride - 1) / s.stride);
+    }
+    off += s.len;
+  }
+  return off;
+}
+int64_t h_last_le(const ra_posmap& m, int64_t P) {
+  int64_t off = 0;
+  int64_t best = -1;
+  for (int i = 0; i < m.nseg; ++i) {
+    const ra_seg& s = m.seg[i];
+    if (s.len > 0 && P >= s.begin) {
+      int64_t k = (P - s.begin) / s.stride;
+      if (k > s.len - 1) k = s.len - 1;
+      best = off + k;
+    }
+    off += s.len;
+  }
+  return best;
+}
+
+// Does any (query, key) pair of these posmaps survive the mask?
+bool step_has_pairs(const ra_problem* p, const ra_posmap& qm, int64_t lq, const ra_posmap& km, int64_t lk) {
+  if (lq == 0 || lk == 0) return false;
+  const int64_t qmax = pos_at(qm, lq - 1);
+  const int64_t kmin = pos_at(km, 0);
+  if (p->num_seqs > 0 && p->cu_seqlens_host) {
+    const int32_t* cu = p->cu_seqlens_host;
+    for (int s = 0; s < p->num_seqs; ++s) {
+      const int64_t a = cu[s], e = cu[s + 1] - 1;
+      if (a > e) continue;
+      const int64_t qi = h_last_le(qm, e), ki = h_first_ge(km, a);
+      if (qi < 0 || ki >= lk) continue;
+      const int64_t qp = pos_at(qm, qi), kp = pos_at(km, ki);
+      if (qp < a || kp > e) continue;
+      if (!p->causal || kp <= qp) return true;
+    }
+    return false;
+  }
+  return !p->causal || kmin <= qmax;
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+// ============================================================================================
+// C ABI
+// ============================================================================================
+
+extern "C" {
+
+const char* ra_status_str(ra_status s) {
+  switch (s) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_INVALID_ARG: return "RA_ERR_INVALID_ARG";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+    case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE";
+  }
+  return "RA_ERR_UNKNOWN";
+}
+
+const char* ra_last_error(void) { return g_err; }
+
+int ra_abi_version(void) { return RA_ABI_VERSION; }
+
+const char* ra_kernel_name(int32_t id) {
+  switch (id) {
+    case K_FWD: return "block_fwd";
+    case K_BWD: return "block_bwd";
+    case K_MERGE: return "lse_merge";
+    case K_PREP: return "bwd_preprocess";
+    case K_FILL: return "fill";
+    case K_CAST: return "cast_bf16";
+    case K_ZERO: return "zero";
+  }
+  return "unknown";
+}
+
+ra_status ra_layout_posmap(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank, ra_posmap* out) {
+  RA_CHECK(out != nullptr, RA_ERR_INVALID_ARG, "out is NULL");
+  return make_posmap(layout, seq_len, world, rank, out);
+}
+
+ra_status ra_layout_positions(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank, int64_t* host_pos_out) {
+  RA_CHECK(host_pos_out != nullptr, RA_ERR_INVALID_ARG, "host_pos_out is NULL");
+  ra_posmap m;
+  ra_status st = make_posmap(layout, seq_len, world, rank, &m);
+  if (st != RA_OK) return st;
+  int64_t a = 0;
+  for (int i = 0; i < m.nseg; ++i)
+    for (int64_t j = 0; j < m.seg[i].len; ++j) host_pos_out[a++] = m.seg[i].begin + j * m.seg[i].stride;
+  return RA_OK;
+}
+
+ra_status ra_timing_begin(int32_t capacity) {
+  RA_CHECK(capacity >= 1 && capacity <= RA_MAX_TIMED_LAUNCHES, RA_ERR_INVALID_ARG, "capacity %d out of range",
+           capacity);
+  Timing& t = g_timing;
+  while ((int)t.ev0.size() < capacity) {
+    hipEvent_t a, b;
+    RA_HIP(hipEventCreate(&a));
+    RA_HIP(hipEventCreate(&b));
+    t.ev0.push_back(a);
+    t.ev1.push_back(b);
+  }
+  t.kid.assign(capacity, -1);
+  t.step.assign(capacity, -1);
+  t.cap = capacity;
+  t.n = 0;
+  t.on = true;
+  return RA_OK;
+}
+
+ra_status ra_timing_end(ra_launch_time* out, int32_t capacity, int32_t* n_out) {
+  Timing& t = g_timing;
+  RA_CHECK(t.on, RA_ERR_INVALID_ARG, "timing was not started");
+  RA_CHECK(n_out != nullptr, RA_ERR_INVALID_ARG, "n_out is NULL");
+  RA_CHECK(out != nullptr || capacity == 0, RA_ERR_INVALID_ARG, "out is NULL");
+  t.on = false;
+  const int n = t.n < capacity ? t.n : capacity;
+  if (t.n > 0) RA_HIP(hipEventSynchronize(t.ev1[t.n - 1]));
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    RA_HIP(hipEventElapsedTime(&ms, t.ev0[i], t.ev1[i]));
+    out[i] = ra_launch_time{t.kid[i], t.step[i], ms};
+  }
+  *n_out = n;
+  t.n = 0;
+  return RA_OK;
+}
+
+ra_status ra_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream) {
+  RA_CHECK(n >= 0, RA_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return RA_OK;
+  RA_CHECK(src != nullptr && dst != nullptr, RA_ERR_INVALID_ARG, "NULL pointer");
+  RA_HIP(timed(K_CAST, -1, (hipStream_t)stream, [&] { return launch_cast(src, dst, n, (hipStream_t)stream); }));
+  return RA_OK;
+}
+
+ra_status ra_block_attn_fwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_posmap qmap, ra_tensor k, ra_tensor v,
+                            int64_t lk, ra_posmap kmap, ra_tensor out_b, float* lse_b, void* stream) {
+  ra_status st = check_problem(prob);
+  if (st != RA_OK) return st;
+  RA_CHECK(lq >= 0 && lq <= kMaxPos && lk >= 0 && lk <= kMaxPos, RA_ERR_INVALID_ARG, "lq/lk out of range");
+  if (lq == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q", q, esz, lq, true)) != RA_OK) return st;
+  if ((st = check_tensor("k", k, esz, lk, lk > 0)) != RA_OK) return st;
+  if ((st = check_tensor("v", v, esz, lk, lk > 0)) != RA_OK) return st;
+  if ((st = check_tensor("out_b", out_b, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_ptr("lse_b", lse_b)) != RA_OK) return st;
+  if ((st = check_posmap("qmap", qmap, lq, prob->seq_len)) != RA_OK) return st;
+  if (lk > 0 && (st = check_posmap("kmap", kmap, lk, prob->seq_len)) != RA_OK) return st;
+
+  FwdArgs a{};
+  a.q = rd(q);
+  a.k = rd(k);
+  a.v = rd(v);
+  a.out = wr(out_b);
+  a.lse = lse_b;
+  a.out_lowp = Tensor4W{nullptr, 0, 0, 0};
+  a.batch = prob->batch;
+  a.heads = prob->heads;
+  a.lq = (int32_t)lq;
+  a.lk = (int32_t)lk;
+  a.qmap = to_dmap(qmap);
+  if (lk > 0) a.kmap = to_dmap(kmap);
+  a.mask = mask_of(prob);
+  a.scale_log2 = scale_of(prob) * 1.4426950408889634f;
+  a.mode = FWD_STORE;
+  a.n_qtiles = ceil_div(lq, FWD_BQ);
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  RA_HIP(timed(K_FWD, -1, s, [&] { return launch_fwd(a, prob->head_dim, bf16, s); }));
+  return RA_OK;
+}
+
+ra_status ra_lse_merge(const ra_problem* prob, int64_t lq, ra_tensor out, float* lse, ra_tensor out_b,
+                       const float* lse_b, void* stream) {
+  ra_status st = check_problem(prob);
+  if (st != RA_OK) return st;
+  RA_CHECK(lq >= 0 && lq <= kMaxPos, RA_ERR_INVALID_ARG, "lq out of range");
+  if (lq == 0) return RA_OK;
+  if ((st = check_tensor("out", out, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_tensor("out_b", out_b, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  if ((st = check_ptr("lse_b", lse_b)) != RA_OK) return st;
+  MergeArgs a{};
+  a.out = wr(out);
+  a.lse = lse;
+  a.out_b = rd(out_b);
+  a.lse_b = lse_b;
+  a.batch = prob->batch;
+  a.heads = prob->heads;
+  a.lq = (int32_t)lq;
+  a.dim = prob->head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  RA_HIP(timed(K_MERGE, -1, s, [&] { return launch_merge(a, s); }));
+  return RA_OK;
+}
+
+ra_status ra_bwd_preprocess(const ra_problem* prob, int64_t lq, ra_tensor out, ra_tensor dout, float* delta,
+                            void* stream) {
+  ra_status st = check_problem(prob);
+  if (st != RA_OK) return st;
+  RA_CHECK(lq >= 0 && lq <= kMaxPos, RA_ERR_INVALID_ARG, "lq out of range");
+  if (lq == 0) return RA_OK;
+  if ((st = check_tensor("out", out, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_tensor("dout", dout, elem_size(prob->dtype), lq, true)) != RA_OK) return st;
+  if ((st = check_ptr("delta", delta)) != RA_OK) return st;
+  PrepArgs a{};
+  a.out = rd(out);
+  a.dout = rd(dout);
+  a.delta = delta;
+  a.batch = prob->batch;
+  a.heads = prob->heads;
+  a.lq = (int32_t)lq;
+  a.dim = prob->head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+  RA_HIP(timed(K_PREP, -1, s, [&] { return launch_prep(a, bf16, s); }));
+  return RA_OK;
+}
+
+static ra_status bwd_args(const ra_problem* prob, ra_tensor q, int64_t lq, const ra_posmap& qmap, Tensor4 k,
+                          Tensor4 v, int64_t lk, const ra_posmap& kmap, ra_tensor dout, const float* lse,
+                          const float* delta, Tensor4W dq, Tensor4W dk, Tensor4W dv, BwdArgs* out) {
+  BwdArgs a{};
+  a.q = rd(q);
+  a.k = k;
+  a.v = v;
+  a.dout = rd(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.batch = prob->batch;
+  a.heads = prob->heads;
+  a.lq = (int32_t)lq;
+  a.lk = (int32_t)lk;
+  a.qmap = to_dmap(qmap);
+  a.kmap = to_dmap(kmap);
+  a.mask = mask_of(prob);
+  a.scale = scale_of(prob);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.n_ktiles = ceil_div(lk, BWD_BK);
+  *out = a;
+  return RA_OK;
+}
+
+ra_status ra_block_attn_bwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_posmap qmap, ra_tensor k, ra_tensor v,
+                            int64_t lk, ra_posmap kmap, ra_tensor dout, const float* lse, const float* delta,
+                            ra_tensor dq_acc, ra_tensor dk_acc, ra_tensor dv_acc, void* stream) {
+  ra_status st = check_problem(prob);
+  if (st != RA_OK) return st;
+  RA_CHECK(lq >= 0 && lq <= kMaxPos && lk >= 0 && lk <= kMaxPos, RA_ERR_INVALID_ARG, "lq/lk out of range");
+  if (lq == 0 || lk == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q", q, esz, lq, true)) != RA_OK) return st;
+  if ((st = check_tensor("k", k, esz, lk, true)) != RA_OK) return st;
+  if ((st = check_tensor("v", v, esz, lk, true)) != RA_OK) return st;
+  if ((st = check_tensor("dout", dout, esz, lq, true)) != RA_OK) return st;
+  if ((st = check_tensor("dq_acc", dq_acc, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_tensor("dk_acc", dk_acc, 4, lk, true)) != RA_OK) return st;
+  if ((st = check_tensor("dv_acc", dv_acc, 4, lk, true)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  if ((st = check_ptr("delta", delta)) != RA_OK) return st;
+  if ((st = check_posmap("qmap", qmap, lq, prob->seq_len)) != RA_OK) return st;
+  if ((st = check_posmap("kmap", kmap, lk, prob->seq_len)) != RA_OK) return st;
+  BwdArgs a;
+  bwd_args(prob, q, lq, qmap, rd(k), rd(v), lk, kmap, dout, lse, delta, wr(dq_acc), wr(dk_acc), wr(dv_acc), &a);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+  RA_HIP(timed(K_BWD, -1, s, [&] { return launch_bwd(a, prob->head_dim, bf16, s); }));
+  return RA_OK;
+}
+
+// ---- virtual ring -------------------------------------------------------------------------
+
+static ra_status ring_common(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, int64_t* L) {
+  ra_status st = check_problem(prob);
+  if (st != RA_OK) return st;
+  RA_CHECK(world >= 1, RA_ERR_INVALID_ARG, "world must be >= 1");
+  RA_CHECK(rank >= 0 && rank < world, RA_ERR_INVALID_ARG, "rank %d out of range [0, %d)", rank, world);
+  ra_posmap m;
+  st = make_posmap(layout, prob->seq_len, world, rank, &m);
+  if (st != RA_OK) return st;
+  *L = prob->seq_len / world;
+  return RA_OK;
+}
+
+ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                      ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, float* lse,
+                      ra_tensor out_lowp, void* stream) {
+  int64_t L = 0;
+  ra_status st = ring_common(prob, layout, world, rank, &L);
+  if (st != RA_OK) return st;
+  if (L == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("k_ring", k_ring, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("v_ring", v_ring, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("out_lowp", out_lowp, esz, L, out_lowp.ptr != nullptr)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
+           "stride_rank must be >= 0 and keep 16-byte alignment");
+
+  ra_posmap qmap;
+  make_posmap(layout, prob->seq_len, world, rank, &qmap);
+  std::vector<int> steps;
+  std::vector<ra_posmap> kmaps(world);
+  for (int s = 0; s < world; ++s) {
+    const int src = ((rank - s) % world + world) % world;
+    make_posmap(layout, prob->seq_len, world, src, &kmaps[s]);
+    if (step_has_pairs(prob, qmap, L, kmaps[s], L)) steps.push_back(s);
+  }
+  if (steps.empty()) steps.push_back(0);  // still writes (0, -inf) rows
+
+  FwdArgs a{};
+  a.q = rd(q_local);
+  a.out = wr(out);
+  a.lse = lse;
+  a.batch = prob->batch;
+  a.heads = prob->heads;
+  a.lq = (int32_t)L;
+  a.lk = (int32_t)L;
+  a.qmap = to_dmap(qmap);
+  a.mask = mask_of(prob);
+  a.scale_log2 = scale_of(prob) * 1.4426950408889634f;
+  a.n_qtiles = ceil_div(L, FWD_BQ);
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  for (size_t i = 0; i < steps.size(); ++i) {
+    const int step = steps[i];
+    const int src = ((rank - step) % world + world) % world;
+    a.k = offset_rd(k_ring, src * stride_rank, esz);
+    a.v = offset_rd(v_ring, src * stride_rank, esz);
+    a.kmap = to_dmap(kmaps[step]);
+    a.mode = (i == 0) ? FWD_STORE : FWD_MERGE;
+    a.out_lowp = (i + 1 == steps.size()) ? wr(out_lowp) : Tensor4W{nullptr, 0, 0, 0};
+    RA_HIP(timed(K_FWD, step, s, [&] { return launch_fwd(a, prob->head_dim, bf16, s); }));
+  }
+  return RA_OK;
+}
+
+size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
+  if (check_problem(prob) != RA_OK || world < 1) return 0;
+  ra_posmap m;
+  if (make_posmap(layout, prob->seq_len, world, 0, &m) != RA_OK) return 0;
+  const int64_t L = prob->seq_len / world;
+  const size_t bytes = (size_t)prob->batch * prob->heads * L * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                      ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, const float* lse,
+                      ra_tensor dout, ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t L = 0;
+  ra_status st = ring_common(prob, layout, world, rank, &L);
+  if (st != RA_OK) return st;
+  if (L == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("k_ring", k_ring, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("v_ring", v_ring, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dout", dout, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dq", dq, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dk_ring", dk_ring, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dv_ring", dv_ring, 4, L, true)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
+           "stride_rank must be >= 0 and keep 16-byte alignment");
+  RA_CHECK(stride_rank_grad >= 0 && stride_rank_grad % 4 == 0, RA_ERR_INVALID_ARG,
+           "stride_rank_grad must be >= 0 and keep 16-byte alignment");
+  const size_t need = ra_ring_workspace_bytes(prob, layout, world);
+  RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
+           "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+
+  ra_posmap qmap;
+  make_posmap(layout, prob->seq_len, world, rank, &qmap);
+  float* delta = (float*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+
+  PrepArgs pa{};
+  pa.out = rd(out);
+  pa.dout = rd(dout);
+  pa.delta = delta;
+  pa.batch = prob->batch;
+  pa.heads = prob->heads;
+  pa.lq = (int32_t)L;
+  pa.dim = prob->head_dim;
+  RA_HIP(timed(K_PREP, -1, s, [&] { return launch_prep(pa, bf16, s); }));
+  Tensor4W dqw = wr(dq);
+  RA_HIP(timed(K_ZERO, -1, s, [&] {
+    return launch_zero(dqw, prob->batch, prob->heads, (int32_t)L, prob->head_dim, s);
+  }));
+  for (int step = 0; step < world; ++step) {
+    const int src = ((rank - step) % world + world) % world;
+    ra_posmap kmap;
+    make_posmap(layout, prob->seq_len, world, src, &kmap);
+    if (!step_has_pairs(prob, qmap, L, kmap, L)) continue;
+    BwdArgs a;
+    bwd_args(prob, q_local, L, qmap, offset_rd(k_ring, src * stride_rank, esz),
+             offset_rd(v_ring, src * stride_rank, esz), L, kmap, dout, lse, delta, dqw,
+             offset_wr(dk_ring, src * stride_rank_grad, 4), offset_wr(dv_ring, src * stride_rank_grad, 4), &a);
+    RA_HIP(timed(K_BWD, step, s, [&] { return launch_bwd(a, prob->head_dim, bf16, s); }));
+  }
+  return RA_OK;
+}
+
+}  // extern "C"

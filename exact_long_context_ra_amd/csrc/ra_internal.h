@@ -1,0 +1,111 @@
+// Internal interface between the host planner (ra_host.cpp) and the gfx950
+// kernels (ra_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Posmap as the kernels see it: int32 positions (seq_len < 2^31 is validated).
+struct DSeg {
+  int32_t begin, stride, len;
+};
+struct DMap {
+  int32_t nseg;
+  DSeg s0, s1;
+  int32_t total;  // s0.len + (nseg == 2 ? s1.len : 0)
+};
+
+// Per-row visibility: key position kp is visible to query position qp iff
+// lo(qp) <= kp <= hi(qp), with lo/hi from the causal flag and cu_seqlens.
+struct MaskSpec {
+  int32_t causal;
+  int32_t nseq;       // 0: one sequence
+  const int32_t* cu;  // device cu_seqlens [nseq+1]
+};
+
+struct Tensor4 {
+  const void* ptr;
+  int64_t sb, st, sh;  // element strides
+};
+struct Tensor4W {
+  void* ptr;
+  int64_t sb, st, sh;
+};
+
+enum FwdMode : int32_t { FWD_STORE = 0, FWD_MERGE = 1 };
+
+struct FwdArgs {
+  Tensor4 q, k, v;
+  Tensor4W out;      // fp32
+  float* lse;        // fp32 [b, h, lq]
+  Tensor4W out_lowp; // optional, ptr may be null; same dtype as q
+  int32_t batch, heads, lq, lk;
+  DMap qmap, kmap;
+  MaskSpec mask;
+  float scale_log2;  // softmax_scale * log2(e)
+  int32_t mode;      // FwdMode
+  int32_t n_qtiles;
+};
+
+struct BwdArgs {
+  Tensor4 q, k, v, dout;
+  const float* lse;    // [b, h, lq] natural log (final)
+  const float* delta;  // [b, h, lq]
+  Tensor4W dq, dk, dv; // fp32 accumulators
+  int32_t batch, heads, lq, lk;
+  DMap qmap, kmap;
+  MaskSpec mask;
+  float scale;         // softmax_scale
+  float scale_log2;    // softmax_scale * log2(e)
+  int32_t n_ktiles;
+};
+
+struct MergeArgs {
+  Tensor4W out;
+  float* lse;
+  Tensor4 out_b;  // fp32
+  const float* lse_b;
+  int32_t batch, heads, lq, dim;
+};
+
+struct PrepArgs {
+  Tensor4 out;   // fp32
+  Tensor4 dout;  // dtype
+  float* delta;  // [b, h, lq]
+  int32_t batch, heads, lq, dim;
+};
+
+struct FillArgs {
+  Tensor4W out;  // fp32, set to 0
+  float* lse;    // set to -inf
+  int32_t batch, heads, lq, dim;
+};
+
+// Kernel ids reported by the timing facility.
+enum KernelId : int32_t {
+  K_FWD = 0,
+  K_BWD = 1,
+  K_MERGE = 2,
+  K_PREP = 3,
+  K_FILL = 4,
+  K_CAST = 5,
+  K_ZERO = 6,
+  K_COUNT = 7
+};
+
+// Tile sizes shared by planner and kernels.
+constexpr int FWD_BQ = 128;  // query rows per forward workgroup
+constexpr int BWD_BK = 128;  // key rows per backward workgroup
+
+// Launchers (ra_kernels.hip).  Return the launch status; the caller checks it.
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_fill(const FillArgs& a, hipStream_t s);
+hipError_t launch_cast(const float* src, void* dst, int64_t n, hipStream_t s);
+hipError_t launch_zero(const Tensor4W& t, int32_t batch, int32_t heads, int32_t rows, int32_t dim,
+                       hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,1016 @@
+// gfx950 (MI355X) kernels for the ring-attention per-device hot path.
+//
+// Forward block step ("Ring Flash Attention" README: each block returns its
+// output and softmax_lse; guijiagi.com Ring Attention article, online-softmax
+// section: running max / running sum rescaling).  One workgroup = 4 waves =
+// 128 query rows; each wave owns 32 query rows and walks the K/V block in
+// tiles of 64 keys staged through LDS.
+//
+// MFMA orientation.  The wave computes S^T = K * Q^T (M = 32 keys, N = 32
+// queries) so that in the MFMA result layout every lane holds ONE query and
+// 16 keys: the row max / row sum of the online softmax are per-lane
+// reductions plus one exchange between the two 32-lane halves.  The A-operand
+// rows (keys) are permuted (bits 2 and 3 of the row index swapped) so that the
+// result registers of each half are 8 consecutive keys, which is exactly the
+// B-operand layout of the next product O^T += V^T * P^T (K-dim = keys).
+// V is therefore staged TRANSPOSED in LDS ([d][key], 16-byte chunks XOR
+// swizzled), so the A operand V^T is one 16-byte LDS read per lane.
+//
+// Backward block step (textbook softmax-attention gradient with P recomputed
+// from the final lse).  One workgroup = 4 waves = 128 keys (32 per wave); it
+// walks the query rows in tiles of 64 staged in LDS (natural and transposed),
+// keeps dK^T and dV^T in registers and adds dQ with fp32 atomics after a
+// round trip of dS through LDS.
+//
+// Masks are evaluated on global token positions (see ra.h): per query row a
+// visible key interval [lo, hi] follows from the causal flag and cu_seqlens;
+// tiles entirely outside it are skipped, tiles entirely inside it run without
+// any per-element mask, and only the remaining tiles are masked per element.
+#include <type_traits>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NT = 256;  // threads per workgroup (4 waves of 64)
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float POS_INF = __builtin_huge_valf();
+constexpr float LN2 = 0.69314718055994531f;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int INT_BIG = 0x7fffffff;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const void* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+
+// A-operand row permutation: swap bits 2 and 3 of the row index.
+__device__ __forceinline__ int row_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// Physical row (within a 32-row block) held by result register v of half hf
+// when the A rows were permuted by row_perm.
+__device__ __forceinline__ int reg_row(int v, int hf) { return (v < 8) ? (8 * hf + v) : (16 + 8 * hf + (v - 8)); }
+
+// Byte offset in a transposed tile with 64 entries (128 bytes) per row: the
+// 16-byte chunk index is XOR-swizzled by the row so that both the 16-byte
+// MFMA-operand reads (32 rows, same chunk) and the 8-byte transposing writes
+// stay (nearly) bank-conflict free.
+__device__ __forceinline__ int tr_off(int row, int col) {
+  int sw = ((row >> 1) ^ (row >> 3)) & 7;
+  return row * 128 + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1);
+}
+
+// ---- posmaps and visibility ---------------------------------------------------------------
+
+__device__ __forceinline__ int map_pos(const DMap& m, int a) {
+  return (a < m.s0.len) ? m.s0.begin + a * m.s0.stride : m.s1.begin + (a - m.s0.len) * m.s1.stride;
+}
+__device__ __forceinline__ int seg_first_ge(const DSeg& s, int P) {
+  if (s.len <= 0) return 0;
+  if (P <= s.begin) return 0;
+  long long last = (long long)s.begin + (long long)(s.len - 1) * s.stride;
+  if (last < P) return s.len;
+  return (int)(((long long)P - s.begin + s.stride - 1) / s.stride);
+}
+__device__ __forceinline__ int seg_last_le(const DSeg& s, int P) {
+  if (s.len <= 0 || P < s.begin) return -1;
+  long long i = ((long long)P - s.begin) / s.stride;
+  return (int)(i < s.len - 1 ? i : s.len - 1);
+}
+// First local index whose position is >= P (total if none).
+__device__ __forceinline__ int first_ge(const DMap& m, int P) {
+  int i = seg_first_ge(m.s0, P);
+  if (i < m.s0.len || m.nseg < 2) return i;
+  return m.s0.len + seg_first_ge(m.s1, P);
+}
+// Last local index whose position is <= P (-1 if none).
+__device__ __forceinline__ int last_le(const DMap& m, int P) {
+  if (m.nseg == 2) {
+    int i = seg_last_le(m.s1, P);
+    if (i >= 0) return m.s0.len + i;
+  }
+  return seg_last_le(m.s0, P);
+}
+
+// Largest k in [0, nseq) with cu[k] <= p.
+__device__ __forceinline__ int seq_index(const MaskSpec& ms, int p) {
+  int lo = 0, hi = ms.nseq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (ms.cu[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct Bounds { int lo, hi; };
+
+// Visible key positions for a query at global position qp.
+__device__ __forceinline__ Bounds row_bounds(const MaskSpec& ms, int qp) {
+  Bounds b;
+  if (ms.nseq > 0) {
+    int k = seq_index(ms, qp);
+    b.lo = ms.cu[k];
+    b.hi = ms.causal ? qp : ms.cu[k + 1] - 1;
+  } else {
+    b.lo = 0;
+    b.hi = ms.causal ? qp : INT_BIG;
+  }
+  return b;
+}
+// Query positions that can see a key at global position kp.
+__device__ __forceinline__ Bounds col_bounds(const MaskSpec& ms, int kp) {
+  Bounds b;
+  if (ms.nseq > 0) {
+    int k = seq_index(ms, kp);
+    b.lo = ms.causal ? kp : ms.cu[k];
+    b.hi = ms.cu[k + 1] - 1;
+  } else {
+    b.lo = ms.causal ? kp : 0;
+    b.hi = INT_BIG;
+  }
+  return b;
+}
+
+// Workgroup id -> logical id, so that consecutive logical ids (same head) land
+// on the same XCD (ids are dispatched round-robin over the 8 XCDs) and share
+// that XCD's L2 for the head's K/V.
+__device__ __forceinline__ int xcd_logical(int bid, int total) {
+  if ((total & 7) != 0) return bid;
+  return (bid & 7) * (total >> 3) + (bid >> 3);
+}
+
+// ============================================================================================
+// Forward
+// ============================================================================================
+
+constexpr int FBK = 64;  // keys per forward tile
+
+template <int D, bool BF16>
+struct FwdCfg {
+  // bf16: K rows padded by 16 bytes; V^T rows of 64 keys, swizzled.
+  // fp32: K rows padded by 2 floats, V rows padded by 4 floats (natural layout).
+  static constexpr int KSTR = BF16 ? (D + 8) * 2 : (D + 2) * 4;
+  static constexpr int VSZ = BF16 ? D * 128 : FBK * (D + 4) * 4;
+  static constexpr int VSTR = (D + 4) * 4;  // fp32 V row stride
+  static constexpr int LDS = FBK * KSTR + VSZ;
+};
+
+template <int D>
+__device__ __forceinline__ void fwd_stage_bf16(const uint16_t* kb, int64_t kst, const uint16_t* vb, int64_t vst,
+                                               int j0, int lk, char* sK, char* sV, int tid) {
+  using C = FwdCfg<D, true>;
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPP = NT / CPR;     // K rows per pass
+  constexpr int KP = FBK / RPP;     // K passes
+  constexpr int VITEMS = (FBK / 4) * CPR;
+  constexpr int VP = (VITEMS + NT - 1) / NT;
+  u32x4 kr[KP];
+#pragma unroll
+  for (int p = 0; p < KP; ++p) {
+    int r = p * RPP + tid / CPR, c = tid % CPR, j = j0 + r;
+    kr[p] = u32x4{0u, 0u, 0u, 0u};
+    if (j < lk) kr[p] = *reinterpret_cast<const u32x4*>(kb + (int64_t)j * kst + c * 8);
+  }
+  u32x4 vr[VP][4];
+#pragma unroll
+  for (int p = 0; p < VP; ++p) {
+    int it = p * NT + tid;
+    int c = it % CPR, kq = it / CPR;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int j = j0 + 4 * kq + i;
+      vr[p][i] = u32x4{0u, 0u, 0u, 0u};
+      if (it < VITEMS && j < lk) vr[p][i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)j * vst + c * 8);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < KP; ++p) {
+    int r = p * RPP + tid / CPR, c = tid % CPR;
+    *reinterpret_cast<u32x4*>(sK + r * C::KSTR + c * 16) = kr[p];
+  }
+#pragma unroll
+  for (int p = 0; p < VP; ++p) {
+    int it = p * NT + tid;
+    if (it < VITEMS) {
+      int c = it % CPR, kq = it / CPR;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        int e = dd >> 1;
+        uint32_t x0 = vr[p][0][e], x1 = vr[p][1][e], x2 = vr[p][2][e], x3 = vr[p][3][e];
+        uint32_t w0, w1;
+        if (dd & 1) {
+          w0 = (x0 >> 16) | (x1 & 0xffff0000u);
+          w1 = (x2 >> 16) | (x3 & 0xffff0000u);
+        } else {
+          w0 = (x0 & 0xffffu) | (x1 << 16);
+          w1 = (x2 & 0xffffu) | (x3 << 16);
+        }
+        *reinterpret_cast<u32x2*>(sV + tr_off(8 * c + dd, 4 * kq)) = u32x2{w0, w1};
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void fwd_stage_f32(const float* kb, int64_t kst, const float* vb, int64_t vst,
+                                              int j0, int lk, char* sK, char* sV, int tid) {
+  using C = FwdCfg<D, false>;
+  constexpr int CPR = D / 4;  // float4 chunks per row
+  constexpr int ITEMS = FBK * CPR;
+  for (int it = tid; it < ITEMS; it += NT) {
+    int r = it / CPR, c = it % CPR, j = j0 + r;
+    f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+    if (j < lk) {
+      kv = *reinterpret_cast<const f32x4*>(kb + (int64_t)j * kst + c * 4);
+      vv = *reinterpret_cast<const f32x4*>(vb + (int64_t)j * vst + c * 4);
+    }
+    float* kd = reinterpret_cast<float*>(sK + r * C::KSTR) + c * 4;
+    *reinterpret_cast<float2*>(kd) = make_float2(kv[0], kv[1]);
+    *reinterpret_cast<float2*>(kd + 2) = make_float2(kv[2], kv[3]);
+    *reinterpret_cast<f32x4*>(sV + r * C::VSTR + c * 16) = vv;
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<D, BF16>;
+  constexpr int NDB = D / 32;  // 32-wide d blocks of the output
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* sK = smem;
+  char* sV = smem + FBK * C::KSTR;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;  // latest (heaviest causal) tiles first
+  const int bh = logical / a.n_qtiles;
+  const int head = bh % a.heads, b = bh / a.heads;
+
+  const int r_first = qt * FWD_BQ;
+  const int r_last = min(a.lq, r_first + FWD_BQ) - 1;
+  const int w_first = r_first + 32 * w;
+  const int w_last = min(r_last, w_first + 31);
+  const bool wave_has_rows = w_first <= r_last;
+  const int row = w_first + l32;
+  const bool row_ok = row <= r_last;
+
+  using TI = typename std::conditional<BF16, uint16_t, float>::type;
+  const TI* qb = reinterpret_cast<const TI*>(a.q.ptr) + b * a.q.sb + head * a.q.sh;
+  const TI* kb = reinterpret_cast<const TI*>(a.k.ptr) + b * a.k.sb + head * a.k.sh;
+  const TI* vb = reinterpret_cast<const TI*>(a.v.ptr) + b * a.v.sb + head * a.v.sh;
+
+  // Query fragments (B operand of S^T = K Q^T), kept in registers.
+  constexpr int NQF = BF16 ? D / 16 : D / 2;
+  typedef typename std::conditional<BF16, bf16x8, float>::type QF;
+  QF qf[NQF];
+  if constexpr (BF16) {
+#pragma unroll
+    for (int c = 0; c < NQF; ++c)
+      qf[c] = row_ok ? ld_bf16x8(qb + (int64_t)row * a.q.st + 16 * c + 8 * hf) : zero_bf16x8();
+  } else {
+#pragma unroll
+    for (int c4 = 0; c4 < D / 4; ++c4) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (row_ok) x = *reinterpret_cast<const f32x4*>(qb + (int64_t)row * a.q.st + 4 * c4);
+      qf[2 * c4] = hf ? x[1] : x[0];
+      qf[2 * c4 + 1] = hf ? x[3] : x[2];
+    }
+  }
+
+  // Visibility bounds: this lane's row, the workgroup's and the wave's extremes.
+  const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, min(row, r_last)));
+  const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
+  const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
+  const Bounds wv_f = row_bounds(a.mask, map_pos(a.qmap, min(w_first, r_last)));
+  const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
+
+  const int kbeg = first_ge(a.kmap, wg_f.lo);
+  const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x16 o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) o[d] = f32x16{};
+  const float sl2 = a.scale_log2;
+
+  if (kbeg < kend) {
+    const int jt0 = kbeg / FBK, jt1 = (kend - 1) / FBK;
+    for (int jt = jt0; jt <= jt1; ++jt) {
+      const int j0 = jt * FBK;
+      if constexpr (BF16)
+        fwd_stage_bf16<D>(kb, a.k.st, vb, a.v.st, j0, a.lk, sK, sV, tid);
+      else
+        fwd_stage_f32<D>(kb, a.k.st, vb, a.v.st, j0, a.lk, sK, sV, tid);
+      __syncthreads();
+
+      const int jl = min(a.lk, j0 + FBK) - 1;
+      const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
+      const bool wave_empty = !wave_has_rows || kmax < wv_f.lo || kmin > wv_l.hi;
+      const bool wave_full = (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
+
+      if (!wave_empty) {
+        // S^T for two 32-key chunks.
+        f32x16 st[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x16 acc = f32x16{};
+          if constexpr (BF16) {
+            const char* kr = sK + (c2 * 32 + row_perm(l32)) * C::KSTR + hf * 16;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(kr + c * 32), qf[c], acc);
+          } else {
+            const float* kr = reinterpret_cast<const float*>(sK + (c2 * 32 + row_perm(l32)) * C::KSTR) + hf;
+#pragma unroll
+            for (int t = 0; t < D / 2; ++t) acc = mfma_f32(kr[2 * t], qf[t], acc);
+          }
+          st[c2] = acc;
+        }
+        if (!wave_full) {
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              int j = j0 + c2 * 32 + reg_row(v, hf);
+              int kp = map_pos(a.kmap, min(j, jl));
+              bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+              st[c2][v] = ok ? st[c2][v] : NEG_INF;
+            }
+          }
+        }
+        // Online softmax in base 2 (scores scaled by softmax_scale*log2(e)).
+        float mx = NEG_INF;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+        const float alpha = ex2(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float p = ex2(__builtin_fmaf(st[c2][v], sl2, -m_use));
+            st[c2][v] = p;
+            rs += p;
+          }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          if constexpr (BF16) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              bf16x8 pb;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
+              const int kcol = c2 * 32 + 16 * u + 8 * hf;
+#pragma unroll
+              for (int d = 0; d < NDB; ++d) o[d] = mfma_bf16(ld_bf16x8(sV + tr_off(d * 32 + l32, kcol)), pb, o[d]);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+              const float* vr = reinterpret_cast<const float*>(sV + (c2 * 32 + reg_row(t, hf)) * C::VSTR) + l32;
+#pragma unroll
+              for (int d = 0; d < NDB; ++d) o[d] = mfma_f32(vr[d * 32], st[c2][t], o[d]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: block-normalise, then store or merge into the fp32 running state.
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  float lse_b, inv;
+  if (l_tot > 0.f) {
+    lse_b = (m_run + __log2f(l_tot)) * LN2;
+    inv = 1.f / l_tot;
+  } else {
+    lse_b = NEG_INF;
+    inv = 0.f;
+  }
+  float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lq + row;
+  float* orow = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)row * a.out.st + head * a.out.sh;
+  float wa = 0.f, wb = inv, lse_new = lse_b;
+  if (a.mode == FWD_MERGE) {
+    const float lse_old = *lse_p;
+    const float mm = fmaxf(lse_old, lse_b);
+    if (mm == NEG_INF) {
+      wa = 0.f; wb = 0.f; lse_new = NEG_INF;
+    } else {
+      const float ea = expf(lse_old - mm), eb = expf(lse_b - mm);
+      const float s = ea + eb;
+      lse_new = mm + logf(s);
+      wa = ea / s;
+      wb = eb / s * inv;
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = d * 32 + 8 * g + 4 * hf;
+      f32x4 val = {o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb};
+      if (a.mode == FWD_MERGE) {
+        f32x4 old = *reinterpret_cast<const f32x4*>(orow + d0);
+        val += wa * old;
+      }
+      *reinterpret_cast<f32x4*>(orow + d0) = val;
+      if (a.out_lowp.ptr) {
+        TI* lp = reinterpret_cast<TI*>(a.out_lowp.ptr) + b * a.out_lowp.sb + (int64_t)row * a.out_lowp.st +
+                 head * a.out_lowp.sh + d0;
+        if constexpr (BF16) {
+          __bf16 t0 = (__bf16)val[0], t1 = (__bf16)val[1], t2 = (__bf16)val[2], t3 = (__bf16)val[3];
+          uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, t0) | ((uint32_t)__builtin_bit_cast(uint16_t, t1) << 16);
+          uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, t2) | ((uint32_t)__builtin_bit_cast(uint16_t, t3) << 16);
+          *reinterpret_cast<u32x2*>(lp) = u32x2{p0, p1};
+        } else {
+          *reinterpret_cast<f32x4*>(lp) = val;
+        }
+      }
+    }
+  }
+  if (hf == 0) *lse_p = lse_new;
+}
+
+// ============================================================================================
+// Backward
+// ============================================================================================
+
+constexpr int BQB = 64;  // query rows per backward inner tile
+
+template <int D, bool BF16>
+struct BwdCfg {
+  static constexpr int QSTR = BF16 ? (D + 8) * 2 : (D + 2) * 4;  // natural Q / dO rows
+  static constexpr int QTSZ = BF16 ? D * 128 : 0;                // transposed Q / dO tiles
+  static constexpr int SSTR = BF16 ? (BWD_BK + 8) * 2 : (BWD_BK + 2) * 4;  // dS rows
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_QT = OFF_Q + BQB * QSTR;
+  static constexpr int OFF_DO = OFF_QT + QTSZ;
+  static constexpr int OFF_DOT = OFF_DO + BQB * QSTR;
+  static constexpr int OFF_DS = OFF_DOT + QTSZ;
+  static constexpr int OFF_LSE = OFF_DS + BQB * SSTR;
+  static constexpr int OFF_DEL = OFF_LSE + BQB * 4;
+  static constexpr int OFF_LO = OFF_DEL + BQB * 4;
+  static constexpr int OFF_HI = OFF_LO + BQB * 4;
+  static constexpr int LDS = OFF_HI + BQB * 4;
+};
+
+// Stage a 64-row tile of a [rows][D] bf16 tensor into LDS, natural and transposed.
+template <int D>
+__device__ __forceinline__ void bwd_stage_bf16(const uint16_t* src, int64_t st, int r0, int lq, char* sN, char* sT,
+                                               int tid) {
+  using C = BwdCfg<D, true>;
+  constexpr int CPR = D / 8;
+  constexpr int ITEMS = (BQB / 4) * CPR;
+  for (int it = tid; it < ITEMS; it += NT) {
+    int c = it % CPR, rq = it / CPR;
+    u32x4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int r = r0 + 4 * rq + i;
+      x[i] = u32x4{0u, 0u, 0u, 0u};
+      if (r < lq) x[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * st + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sN + (4 * rq + i) * C::QSTR + c * 16) = x[i];
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      int e = dd >> 1;
+      uint32_t w0, w1;
+      if (dd & 1) {
+        w0 = (x[0][e] >> 16) | (x[1][e] & 0xffff0000u);
+        w1 = (x[2][e] >> 16) | (x[3][e] & 0xffff0000u);
+      } else {
+        w0 = (x[0][e] & 0xffffu) | (x[1][e] << 16);
+        w1 = (x[2][e] & 0xffffu) | (x[3][e] << 16);
+      }
+      *reinterpret_cast<u32x2*>(sT + tr_off(8 * c + dd, 4 * rq)) = u32x2{w0, w1};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void bwd_stage_f32(const float* src, int64_t st, int r0, int lq, char* sN, int tid) {
+  using C = BwdCfg<D, false>;
+  constexpr int CPR = D / 4;
+  constexpr int ITEMS = BQB * CPR;
+  for (int it = tid; it < ITEMS; it += NT) {
+    int r = it / CPR, c = it % CPR;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (r0 + r < lq) x = *reinterpret_cast<const f32x4*>(src + (int64_t)(r0 + r) * st + c * 4);
+    float* d = reinterpret_cast<float*>(sN + r * C::QSTR) + c * 4;
+    *reinterpret_cast<float2*>(d) = make_float2(x[0], x[1]);
+    *reinterpret_cast<float2*>(d + 2) = make_float2(x[2], x[3]);
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
+  using C = BwdCfg<D, BF16>;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* sQ = smem + C::OFF_Q;
+  char* sQt = smem + C::OFF_QT;
+  char* sDO = smem + C::OFF_DO;
+  char* sDOt = smem + C::OFF_DOT;
+  char* sDS = smem + C::OFF_DS;
+  float* sLse = reinterpret_cast<float*>(smem + C::OFF_LSE);
+  float* sDel = reinterpret_cast<float*>(smem + C::OFF_DEL);
+  int* sLo = reinterpret_cast<int*>(smem + C::OFF_LO);
+  int* sHi = reinterpret_cast<int*>(smem + C::OFF_HI);
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int kt = logical % a.n_ktiles;  // earliest (heaviest causal) key tiles first
+  const int bh = logical / a.n_ktiles;
+  const int head = bh % a.heads, b = bh / a.heads;
+
+  using TI = typename std::conditional<BF16, uint16_t, float>::type;
+  const TI* qb = reinterpret_cast<const TI*>(a.q.ptr) + b * a.q.sb + head * a.q.sh;
+  const TI* kb = reinterpret_cast<const TI*>(a.k.ptr) + b * a.k.sb + head * a.k.sh;
+  const TI* vb = reinterpret_cast<const TI*>(a.v.ptr) + b * a.v.sb + head * a.v.sh;
+  const TI* dob = reinterpret_cast<const TI*>(a.dout.ptr) + b * a.dout.sb + head * a.dout.sh;
+  const float* lse_b = a.lse + ((int64_t)b * a.heads + head) * a.lq;
+  const float* del_b = a.delta + ((int64_t)b * a.heads + head) * a.lq;
+  float* dqb = reinterpret_cast<float*>(a.dq.ptr) + b * a.dq.sb + head * a.dq.sh;
+
+  const int k_first = kt * BWD_BK;
+  const int k_last = min(a.lk, k_first + BWD_BK) - 1;
+  const int kw0 = k_first + 32 * w;
+  const int kw_last = min(k_last, kw0 + 31);
+  const bool wave_has_keys = kw0 <= k_last;
+  const int key = kw0 + l32;
+  const bool key_ok = key <= k_last;
+  const int kpos = map_pos(a.kmap, min(key, k_last));
+
+  // Key/value fragments (B operands of S = Q K^T and dP = dO V^T).
+  constexpr int NKF = BF16 ? D / 16 : D / 2;
+  typedef typename std::conditional<BF16, bf16x8, float>::type KF;
+  KF kf[NKF], vf[NKF];
+  if constexpr (BF16) {
+#pragma unroll
+    for (int c = 0; c < NKF; ++c) {
+      kf[c] = key_ok ? ld_bf16x8(kb + (int64_t)key * a.k.st + 16 * c + 8 * hf) : zero_bf16x8();
+      vf[c] = key_ok ? ld_bf16x8(vb + (int64_t)key * a.v.st + 16 * c + 8 * hf) : zero_bf16x8();
+    }
+  } else {
+#pragma unroll
+    for (int c4 = 0; c4 < D / 4; ++c4) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+      if (key_ok) {
+        x = *reinterpret_cast<const f32x4*>(kb + (int64_t)key * a.k.st + 4 * c4);
+        y = *reinterpret_cast<const f32x4*>(vb + (int64_t)key * a.v.st + 4 * c4);
+      }
+      kf[2 * c4] = hf ? x[1] : x[0];
+      kf[2 * c4 + 1] = hf ? x[3] : x[2];
+      vf[2 * c4] = hf ? y[1] : y[0];
+      vf[2 * c4 + 1] = hf ? y[3] : y[2];
+    }
+  }
+
+  // dQ assignment: (query block, d block) pairs of the 64 x D dQ tile.
+  constexpr int PAIRS = 2 * NDB / 4;  // per wave: 2 for D=128, 1 for D=64
+  const int dq_db = (D == 128) ? w : (w & 1);
+  const int dq_qb0 = (D == 128) ? 0 : (w >> 1);
+  // K^T fragments for dQ = dS K (bf16: 8 consecutive keys for one d per lane).
+  bf16x8 ktf[BF16 ? BWD_BK / 16 : 1];
+  if constexpr (BF16) {
+    const int dcol = dq_db * 32 + l32;
+#pragma unroll
+    for (int jj = 0; jj < BWD_BK / 16; ++jj) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int kk = k_first + 16 * jj + 8 * hf + i;
+        uint16_t bits = (kk <= k_last) ? kb[(int64_t)kk * a.k.st + dcol] : (uint16_t)0;
+        ktf[jj][i] = __builtin_bit_cast(__bf16, bits);
+      }
+    }
+  }
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    dk[d] = f32x16{};
+    dv[d] = f32x16{};
+  }
+
+  // Query rows that can see any key of this tile.
+  const Bounds cf = col_bounds(a.mask, map_pos(a.kmap, k_first));
+  const Bounds cl = col_bounds(a.mask, map_pos(a.kmap, k_last));
+  const int rbeg = first_ge(a.qmap, cf.lo);
+  const int rend = min(a.lq, last_le(a.qmap, cl.hi) + 1);
+  const int kwmin = map_pos(a.kmap, min(kw0, k_last)), kwmax = map_pos(a.kmap, kw_last);
+  const float sl2 = a.scale_log2;
+
+  if (rbeg < rend) {
+    const int qt0 = rbeg / BQB, qt1 = (rend - 1) / BQB;
+    for (int qt = qt0; qt <= qt1; ++qt) {
+      const int r0 = qt * BQB;
+      const int nrows = min(a.lq - r0, BQB);
+      if constexpr (BF16) {
+        bwd_stage_bf16<D>(qb, a.q.st, r0, a.lq, sQ, sQt, tid);
+        bwd_stage_bf16<D>(dob, a.dout.st, r0, a.lq, sDO, sDOt, tid);
+      } else {
+        bwd_stage_f32<D>(qb, a.q.st, r0, a.lq, sQ, tid);
+        bwd_stage_f32<D>(dob, a.dout.st, r0, a.lq, sDO, tid);
+      }
+      if (tid < BQB) {
+        const int r = r0 + tid;
+        if (r < a.lq) {
+          const float l = lse_b[r];
+          sLse[tid] = (l == NEG_INF) ? POS_INF : l * LOG2E;
+          sDel[tid] = del_b[r];
+          const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, r));
+          sLo[tid] = rb.lo;
+          sHi[tid] = rb.hi;
+        } else {
+          sLse[tid] = POS_INF;
+          sDel[tid] = 0.f;
+          sLo[tid] = INT_BIG;
+          sHi[tid] = -1;
+        }
+      }
+      __syncthreads();
+
+      const int lo_f = sLo[0], hi_f = sHi[0], lo_l = sLo[nrows - 1], hi_l = sHi[nrows - 1];
+      const bool wave_empty = !wave_has_keys || kwmax < lo_f || kwmin > hi_l;
+      const bool wave_full = (kw0 + 32 <= a.lk) && kwmin >= lo_l && kwmax <= hi_f;
+
+      if (!wave_empty) {
+        // S = Q K^T (rows permuted), P = exp2(S*scale*log2e - lse*log2e).
+        f32x16 p[2];
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+          f32x16 acc = f32x16{};
+          if constexpr (BF16) {
+            const char* qr = sQ + (qbk * 32 + row_perm(l32)) * C::QSTR + hf * 16;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(qr + c * 32), kf[c], acc);
+          } else {
+            const float* qr = reinterpret_cast<const float*>(sQ + (qbk * 32 + row_perm(l32)) * C::QSTR) + hf;
+#pragma unroll
+            for (int t = 0; t < D / 2; ++t) acc = mfma_f32(qr[2 * t], kf[t], acc);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = qbk * 32 + reg_row(v, hf);
+            float e = ex2(__builtin_fmaf(acc[v], sl2, -sLse[q]));
+            if (!wave_full) {
+              const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
+              e = ok ? e : 0.f;
+            }
+            p[qbk][v] = e;
+          }
+        }
+        // dP = dO V^T (rows permuted), dS = P * (dP - delta).
+        f32x16 ds[2];
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+          f32x16 acc = f32x16{};
+          if constexpr (BF16) {
+            const char* dr = sDO + (qbk * 32 + row_perm(l32)) * C::QSTR + hf * 16;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(dr + c * 32), vf[c], acc);
+          } else {
+            const float* dr = reinterpret_cast<const float*>(sDO + (qbk * 32 + row_perm(l32)) * C::QSTR) + hf;
+#pragma unroll
+            for (int t = 0; t < D / 2; ++t) acc = mfma_f32(dr[2 * t], vf[t], acc);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = qbk * 32 + reg_row(v, hf);
+            ds[qbk][v] = p[qbk][v] * (acc[v] - sDel[q]);
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (K-dim = query rows).
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+          if constexpr (BF16) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              bf16x8 pb, sb;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                pb[i] = (__bf16)p[qbk][8 * u + i];
+                sb[i] = (__bf16)ds[qbk][8 * u + i];
+              }
+              const int qcol = qbk * 32 + 16 * u + 8 * hf;
+#pragma unroll
+              for (int d = 0; d < NDB; ++d) {
+                dv[d] = mfma_bf16(ld_bf16x8(sDOt + tr_off(d * 32 + l32, qcol)), pb, dv[d]);
+                dk[d] = mfma_bf16(ld_bf16x8(sQt + tr_off(d * 32 + l32, qcol)), sb, dk[d]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+              const int q = qbk * 32 + reg_row(t, hf);
+              const float* dor = reinterpret_cast<const float*>(sDO + q * C::QSTR) + l32;
+              const float* qr = reinterpret_cast<const float*>(sQ + q * C::QSTR) + l32;
+#pragma unroll
+              for (int d = 0; d < NDB; ++d) {
+                dv[d] = mfma_f32(dor[d * 32], p[qbk][t], dv[d]);
+                dk[d] = mfma_f32(qr[d * 32], ds[qbk][t], dk[d]);
+              }
+            }
+          }
+        }
+        // dS -> LDS [query][key] for the dQ product.
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = qbk * 32 + reg_row(v, hf);
+            if constexpr (BF16)
+              *reinterpret_cast<__bf16*>(sDS + q * C::SSTR + (32 * w + l32) * 2) = (__bf16)ds[qbk][v];
+            else
+              *reinterpret_cast<float*>(sDS + q * C::SSTR + (32 * w + l32) * 4) = ds[qbk][v];
+          }
+      } else {
+        // A wave with nothing visible still provides its (zero) dS columns.
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = qbk * 32 + reg_row(v, hf);
+            if constexpr (BF16)
+              *reinterpret_cast<uint16_t*>(sDS + q * C::SSTR + (32 * w + l32) * 2) = 0;
+            else
+              *reinterpret_cast<float*>(sDS + q * C::SSTR + (32 * w + l32) * 4) = 0.f;
+          }
+      }
+      __syncthreads();
+
+      // dQ[tile rows] += scale * dS K  (M = query rows, N = d, K-dim = this tile's keys).
+#pragma unroll
+      for (int pi = 0; pi < PAIRS; ++pi) {
+        const int qbk = dq_qb0 + pi;
+        f32x16 acc = f32x16{};
+        if constexpr (BF16) {
+          const char* sr = sDS + (qbk * 32 + l32) * C::SSTR + hf * 16;
+#pragma unroll
+          for (int jj = 0; jj < BWD_BK / 16; ++jj) acc = mfma_bf16(ld_bf16x8(sr + jj * 32), ktf[jj], acc);
+        } else {
+          const float* sr = reinterpret_cast<const float*>(sDS + (qbk * 32 + l32) * C::SSTR) + hf;
+          const int dcol = dq_db * 32 + l32;
+          for (int t = 0; t < BWD_BK / 2; ++t) {
+            const int kk = k_first + 2 * t + hf;
+            const float kv = (kk <= k_last) ? kb[(int64_t)kk * a.k.st + dcol] : 0.f;
+            acc = mfma_f32(sr[2 * t], kv, acc);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int q = qbk * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+          const int r = r0 + q;
+          if (r < a.lq) atomicAdd(dqb + (int64_t)r * a.dq.st + dq_db * 32 + l32, acc[v] * a.scale);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: dK += scale * dK^T, dV += dV^T (fp32 read-modify-write; this
+  // workgroup owns these key rows for the whole launch).
+  if (!key_ok) return;
+  float* dkr = reinterpret_cast<float*>(a.dk.ptr) + b * a.dk.sb + (int64_t)key * a.dk.st + head * a.dk.sh;
+  float* dvr = reinterpret_cast<float*>(a.dv.ptr) + b * a.dv.sb + (int64_t)key * a.dv.st + head * a.dv.sh;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = d * 32 + 8 * g + 4 * hf;
+      f32x4 x = *reinterpret_cast<const f32x4*>(dkr + d0);
+      f32x4 y = *reinterpret_cast<const f32x4*>(dvr + d0);
+      x += a.scale * f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]};
+      y += f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(dkr + d0) = x;
+      *reinterpret_cast<f32x4*>(dvr + d0) = y;
+    }
+}
+
+// ============================================================================================
+// HBM-bound helpers
+// ============================================================================================
+
+// Standalone lse merge: one thread per (row, 4 consecutive d).
+__global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a) {
+  const int64_t per_row = a.dim / 4;
+  const int64_t total = (int64_t)a.batch * a.lq * a.heads * per_row;
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i >= total) return;
+  const int c = (int)(i % per_row);
+  int64_t rr = i / per_row;
+  const int h = (int)(rr % a.heads);
+  rr /= a.heads;
+  const int t = (int)(rr % a.lq);
+  const int b = (int)(rr / a.lq);
+  float* lse_p = a.lse + ((int64_t)b * a.heads + h) * a.lq + t;
+  const float la = *lse_p;
+  const float lb = a.lse_b[((int64_t)b * a.heads + h) * a.lq + t];
+  const float mm = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f;
+  if (mm != NEG_INF) {
+    const float ea = expf(la - mm), eb = expf(lb - mm);
+    const float s = ea + eb;
+    wa = ea / s;
+    wb = eb / s;
+  }
+  float* o = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)t * a.out.st + h * a.out.sh + 4 * c;
+  const float* ob =
+      reinterpret_cast<const float*>(a.out_b.ptr) + b * a.out_b.sb + (int64_t)t * a.out_b.st + h * a.out_b.sh + 4 * c;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(o);
+  const f32x4 y = *reinterpret_cast<const f32x4*>(ob);
+  *reinterpret_cast<f32x4*>(o) = wa * x + wb * y;
+}
+
+// Second pass of the standalone merge: the lse is rewritten only after every
+// output chunk of the row has read the old value (previous launch).
+
+__global__ __launch_bounds__(NT) void merge_lse_kernel(MergeArgs a) {
+  const int64_t total = (int64_t)a.batch * a.heads * a.lq;
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i >= total) return;
+  const float la = a.lse[i], lb = a.lse_b[i];
+  const float mm = fmaxf(la, lb);
+  a.lse[i] = (mm == NEG_INF) ? NEG_INF : mm + logf(expf(la - mm) + expf(lb - mm));
+}
+
+// delta[b, h, t] = sum_d dout * out.  16 lanes per row.
+template <bool BF16>
+__global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
+  const int64_t rows = (int64_t)a.batch * a.lq * a.heads;
+  const int64_t rid = (int64_t)blockIdx.x * (NT / 16) + threadIdx.x / 16;
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  int b = 0, t = 0, h = 0;
+  if (rid < rows) {
+    h = (int)(rid % a.heads);
+    int64_t rr = rid / a.heads;
+    t = (int)(rr % a.lq);
+    b = (int)(rr / a.lq);
+    const float* o = reinterpret_cast<const float*>(a.out.ptr) + b * a.out.sb + (int64_t)t * a.out.st + h * a.out.sh;
+    for (int d = sub * 4; d < a.dim; d += 64) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(o + d);
+      float y0, y1, y2, y3;
+      if constexpr (BF16) {
+        const uint16_t* g = reinterpret_cast<const uint16_t*>(a.dout.ptr) + b * a.dout.sb + (int64_t)t * a.dout.st +
+                            h * a.dout.sh + d;
+        const u32x2 u = *reinterpret_cast<const u32x2*>(g);
+        y0 = __uint_as_float(u[0] << 16);
+        y1 = __uint_as_float(u[0] & 0xffff0000u);
+        y2 = __uint_as_float(u[1] << 16);
+        y3 = __uint_as_float(u[1] & 0xffff0000u);
+      } else {
+        const f32x4 y = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.dout.ptr) + b * a.dout.sb +
+                                                        (int64_t)t * a.dout.st + h * a.dout.sh + d);
+        y0 = y[0]; y1 = y[1]; y2 = y[2]; y3 = y[3];
+      }
+      acc += x[0] * y0 + x[1] * y1 + x[2] * y2 + x[3] * y3;
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (rid < rows && sub == 0) a.delta[((int64_t)b * a.heads + h) * a.lq + t] = acc;
+}
+
+// out rows = 0 (fp32, 4 at a time), lse = -inf.
+__global__ __launch_bounds__(NT) void fill_kernel(FillArgs a) {
+  const int64_t per_row = a.dim / 4;
+  const int64_t total = (int64_t)a.batch * a.lq * a.heads * per_row;
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i < total) {
+    const int c = (int)(i % per_row);
+    int64_t rr = i / per_row;
+    const int h = (int)(rr % a.heads);
+    rr /= a.heads;
+    const int t = (int)(rr % a.lq);
+    const int b = (int)(rr / a.lq);
+    float* o = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)t * a.out.st + h * a.out.sh + 4 * c;
+    *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (i < (int64_t)a.batch * a.heads * a.lq) a.lse[i] = NEG_INF;
+}
+
+__global__ __launch_bounds__(NT) void zero_kernel(Tensor4W t, int32_t batch, int32_t heads, int32_t rows, int32_t dim) {
+  const int64_t per_row = dim / 4;
+  const int64_t total = (int64_t)batch * rows * heads * per_row;
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i >= total) return;
+  const int c = (int)(i % per_row);
+  int64_t rr = i / per_row;
+  const int h = (int)(rr % heads);
+  rr /= heads;
+  const int r = (int)(rr % rows);
+  const int b = (int)(rr / rows);
+  float* o = reinterpret_cast<float*>(t.ptr) + b * t.sb + (int64_t)r * t.st + h * t.sh + 4 * c;
+  *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+__global__ __launch_bounds__(NT) void cast_kernel(const float* src, uint16_t* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (i < n) dst[i] = __builtin_bit_cast(uint16_t, (__bf16)src[i]);
+}
+
+inline unsigned blocks_for(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
+
+}  // namespace
+
+// ============================================================================================
+// Launchers
+// ============================================================================================
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
+  if (grid == 0) return hipSuccess;
+  if (bf16) {
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_kernel<128, true>), dim3(grid), dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<64, true>), dim3(grid), dim3(NT), 0, s, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_kernel<128, false>), dim3(grid), dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<64, false>), dim3(grid), dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
+  if (grid == 0) return hipSuccess;
+  if (bf16) {
+    if (head_dim == 128) hipLaunchKernelGGL((bwd_kernel<128, true>), dim3(grid), dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((bwd_kernel<64, true>), dim3(grid), dim3(NT), 0, s, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((bwd_kernel<128, false>), dim3(grid), dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((bwd_kernel<64, false>), dim3(grid), dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  const int64_t n_out = (int64_t)a.batch * a.lq * a.heads * (a.dim / 4);
+  const int64_t n_lse = (int64_t)a.batch * a.heads * a.lq;
+  if (n_out == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(n_out)), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_lse_kernel, dim3(blocks_for(n_lse)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.lq * a.heads;
+  if (rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows + NT / 16 - 1) / (NT / 16));
+  if (bf16) hipLaunchKernelGGL(prep_kernel<true>, dim3(grid), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL(prep_kernel<false>, dim3(grid), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(const FillArgs& a, hipStream_t s) {
+  const int64_t n_out = (int64_t)a.batch * a.lq * a.heads * (a.dim / 4);
+  const int64_t n_lse = (int64_t)a.batch * a.heads * a.lq;
+  const int64_t n = n_out > n_lse ? n_out : n_lse;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(n)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* src, void* dst, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel, dim3(blocks_for(n)), dim3(NT), 0, s, src, reinterpret_cast<uint16_t*>(dst), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(const Tensor4W& t, int32_t batch, int32_t heads, int32_t rows, int32_t dim, hipStream_t s) {
+  const int64_t n = (int64_t)batch * rows * heads * (dim / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks_for(n)), dim3(NT), 0, s, t, batch, heads, rows, dim);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,203 @@
+/*
+ * ra.h -- C ABI of the MI355X (gfx950) ring-attention per-device library.
+ *
+ * What is computed.  Exact softmax attention of a device's local query chunk
+ * against a sequence of key/value blocks, as in Ring Attention: every block
+ * step produces a block-normalised output together with its softmax
+ * log-sum-exp ("softmax_lse"), and the step results are combined through
+ * their lse into an fp32 running output ("Ring Flash Attention" README on
+ * github.com/zhuzilin/ring-flash-attention: the lse of each block is what
+ * makes blockwise results combinable; its "Limits" section: combining bf16
+ * block outputs loses accuracy, hence fp32 accumulation here).  The ring
+ * itself is virtual: all N steps of one rank's share run one after another on
+ * this GPU, with every rank's K/V block resident in device memory.
+ *
+ * Conventions (apply to every entry point):
+ *  - Every call returns ra_status.  On any non-OK status nothing has been
+ *    enqueued and no output has been written; ra_last_error() returns a
+ *    thread-local message describing the failure.
+ *  - Tensors are caller-owned DEVICE memory.  The library never allocates or
+ *    frees device memory; calls that need scratch take a caller workspace.
+ *  - Calls are asynchronous on the caller's stream (a hipStream_t passed as
+ *    void*, NULL = the null stream).  Buffers must stay alive and unmodified
+ *    until the stream has finished the work.
+ *  - Q/K/V/dO and outputs are token-major [batch, tokens, heads, head_dim]
+ *    described by ra_tensor: element strides for batch, token and head; the
+ *    head_dim axis is contiguous.  Base pointers and all strides must keep
+ *    every row 16-byte aligned.  lse/delta buffers are dense [batch, heads, tokens].
+ *  - Token positions are GLOBAL positions in the full sequence (a posmap maps
+ *    a local token index to its global position).  Masks are evaluated on
+ *    global positions: key j is visible to query i iff
+ *      (!causal || pos_k(j) <= pos_q(i)) && seq(pos_k(j)) == seq(pos_q(i)),
+ *    where seq() is the packed-sequence index given by cu_seqlens (a single
+ *    array shared by q and k/v, as the reference's varlen API has it).
+ *  - A row with no visible key gets out = 0 and lse = -inf.
+ *  - lse is the natural log of sum_j exp(scale * <q_i, k_j>) over visible j.
+ *  - Supported: head_dim 64 or 128; dtype bf16 (MFMA bf16, fp32 accumulate)
+ *    or fp32 (fp32 MFMA throughout).  seq_len < 2^31.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_ABI_VERSION 1
+#define RA_MAX_TIMED_LAUNCHES 65536
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1, /* a pointer, size, stride or enum is not acceptable */
+  RA_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. head_dim 96) */
+  RA_ERR_HIP = 3,         /* a HIP runtime call failed (message has the HIP error) */
+  RA_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
+} ra_status;
+
+/* Token-to-device layouts.
+ *  CONTIGUOUS: rank r owns the r-th of N equal consecutive chunks.
+ *  ZIGZAG:     the sequence is cut into 2N equal chunks; rank r owns chunk r
+ *              followed by chunk 2N-1-r (balances causal work; "zigzag ring"
+ *              of the ring-flash-attention README).
+ *  STRIPE:     token t lives on rank t mod N ("Striped Ring Attention" section
+ *              of the guijiagi.com Ring Attention article; Striped Attention
+ *              abstract on briefgpt.xyz). */
+typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_ZIGZAG = 1, RA_LAYOUT_STRIPE = 2 } ra_layout;
+
+typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
+
+/* One arithmetic run of a posmap: `len` local tokens whose global positions
+ * are begin, begin+stride, ...  */
+typedef struct { int64_t begin, stride, len; } ra_seg;
+
+/* Local token index -> global position: the segments are concatenated in
+ * local order.  Positions must be strictly increasing over the whole map
+ * (true for all three layouts), stride >= 1, nseg in {1, 2}. */
+typedef struct { int32_t nseg; ra_seg seg[2]; } ra_posmap;
+
+/* A token-major tensor: element (b, t, h, d) lives at
+ * ptr + b*stride_b + t*stride_t + h*stride_h + d (in elements). */
+typedef struct { void* ptr; int64_t stride_b, stride_t, stride_h; } ra_tensor;
+
+typedef struct {
+  int32_t batch, heads, head_dim; /* q and k/v share `heads` (no GQA) */
+  ra_dtype dtype;                 /* element type of q, k, v, dout */
+  float softmax_scale;            /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t causal;                 /* nonzero: mask by global positions */
+  const int32_t* cu_seqlens;      /* DEVICE int32 [num_seqs+1] global offsets, or NULL (one sequence) */
+  const int32_t* cu_seqlens_host; /* optional HOST copy of the same array: when given it is validated
+                                     (cu[0]=0, non-decreasing, cu[num_seqs]=seq_len) and used to skip
+                                     ring steps with no visible pair; may be NULL */
+  int32_t num_seqs;               /* entries of cu_seqlens minus one; batch must be 1 when > 0 */
+  int64_t seq_len;                /* S: global tokens of the whole (virtual) ring */
+} ra_problem;
+
+/* ---- block level ------------------------------------------------------------------------ */
+
+/* Attention of q (lq local tokens, positions qmap) against one K/V block (lk tokens,
+ * positions kmap).  out_b (fp32 [b, lq, h, d]) and lse_b (fp32 [b, h, lq]) are
+ * OVERWRITTEN with the block-normalised output and its lse (natural log).
+ * This is one step of the ring ("Ring Flash Attention" README: each block's kernel
+ * returns out and softmax_lse). */
+ra_status ra_block_attn_fwd(const ra_problem* prob,
+                            ra_tensor q, int64_t lq, ra_posmap qmap,
+                            ra_tensor k, ra_tensor v, int64_t lk, ra_posmap kmap,
+                            ra_tensor out_b, float* lse_b, void* stream);
+
+/* In place, fp32: (out, lse) <- merge((out, lse), (out_b, lse_b)) with
+ *   lse' = log(exp(lse) + exp(lse_b)),
+ *   out' = exp(lse - lse') * out + exp(lse_b - lse') * out_b,
+ * a side with lse = -inf contributing nothing (online-softmax update of the
+ * guijiagi.com Ring Attention article, section on online softmax, written with
+ * each side's (max, sum) state taken as (lse, 1)).  out/out_b fp32 [b, lq, h, d];
+ * lse/lse_b fp32 [b, h, lq]. */
+ra_status ra_lse_merge(const ra_problem* prob, int64_t lq,
+                       ra_tensor out, float* lse, ra_tensor out_b, const float* lse_b,
+                       void* stream);
+
+/* delta[b, h, i] = sum_d dout[b, i, h, d] * out[b, i, h, d] (out fp32 final output,
+ * dout in prob->dtype).  First step of the backward (textbook softmax gradient;
+ * the pages give no backward). */
+ra_status ra_bwd_preprocess(const ra_problem* prob, int64_t lq, ra_tensor out, ra_tensor dout,
+                            float* delta, void* stream);
+
+/* Backward of one block step using the FINAL lse and delta of the rows:
+ *   P = exp(scale*q.k - lse) on visible pairs, dV += P^T dO, dS = P*(dO.V^T - delta),
+ *   dQ += scale*dS K, dK += scale*dS^T Q.
+ * dq_acc (fp32 [b, lq, h, d]), dk_acc and dv_acc (fp32 [b, lk, h, d]) are ACCUMULATED
+ * (+=).  dq_acc is updated with fp32 atomics; concurrent calls on other streams that
+ * touch the same dk_acc/dv_acc rows race. */
+ra_status ra_block_attn_bwd(const ra_problem* prob,
+                            ra_tensor q, int64_t lq, ra_posmap qmap,
+                            ra_tensor k, ra_tensor v, int64_t lk, ra_posmap kmap,
+                            ra_tensor dout, const float* lse, const float* delta,
+                            ra_tensor dq_acc, ra_tensor dk_acc, ra_tensor dv_acc,
+                            void* stream);
+
+/* ---- virtual ring (one rank's share) ----------------------------------------------------- */
+
+/* Forward of rank `rank`'s share of an N-rank ring in `layout` ("Ring Attention"
+ * article on guijiagi.com, detailed-flow section: at step s the rank attends to the
+ * block of rank (rank - s) mod N).
+ *  q_local: [b, S/N, h, d] in prob->dtype, local tokens in layout order.
+ *  k_ring, v_ring: block n of rank n at ptr + n*stride_rank elements, each [b, S/N, h, d].
+ *  out: fp32 [b, S/N, h, d] and lse: fp32 [b, h, S/N], OVERWRITTEN.
+ *  out_lowp: optional copy of the final output in prob->dtype (ptr NULL = none).
+ * Each step's block result is folded into out/lse by the lse merge inside the
+ * attention kernel's epilogue (fp32 throughout); steps without any visible pair
+ * are not launched. */
+ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                      ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
+                      ra_tensor out, float* lse, ra_tensor out_lowp, void* stream);
+
+/* Backward of rank `rank`'s share.  out/lse are that rank's FINAL forward results
+ * (as written by ra_ring_fwd), dout its output gradient (prob->dtype).
+ *  dq: fp32 [b, S/N, h, d], OVERWRITTEN.
+ *  dk_ring, dv_ring: fp32, block n at ptr + n*stride_rank_grad elements, each
+ *  [b, S/N, h, d]; ACCUMULATED (+=) with this rank's contribution, so that running
+ *  every rank into the same buffers yields the full gradients.
+ *  workspace: device memory of at least ra_ring_workspace_bytes() bytes. */
+ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                      ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
+                      ra_tensor out, const float* lse, ra_tensor dout,
+                      ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace ra_ring_bwd needs (0 on invalid input). */
+size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world);
+
+/* ---- utilities ---------------------------------------------------------------------------- */
+
+/* host_pos_out[a] = global position of local token a of `rank` (S/N entries, host memory). */
+ra_status ra_layout_positions(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank,
+                              int64_t* host_pos_out);
+
+/* The posmap ra_ring_fwd/bwd use for `rank` (host struct). */
+ra_status ra_layout_posmap(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank,
+                           ra_posmap* out);
+
+/* dst[i] = bf16 round-to-nearest-even of src[i], i < n (device pointers). */
+ra_status ra_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
+
+/* Kernel timing.  Between ra_timing_begin and ra_timing_end every kernel the library
+ * launches from the calling thread is bracketed by a pair of HIP events recorded on the
+ * launch stream.  ra_timing_end waits for the last event and writes, per launch, the
+ * kernel id, the ring step (-1 outside a ring call) and the elapsed milliseconds.
+ * At most `capacity` (<= RA_MAX_TIMED_LAUNCHES) launches are recorded. */
+typedef struct { int32_t kernel_id; int32_t step; float ms; } ra_launch_time;
+ra_status ra_timing_begin(int32_t capacity);
+ra_status ra_timing_end(ra_launch_time* out, int32_t capacity, int32_t* n_out);
+const char* ra_kernel_name(int32_t kernel_id);
+
+const char* ra_status_str(ra_status s);
+const char* ra_last_error(void);
+int ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

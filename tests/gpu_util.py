@@ -1,0 +1,85 @@
+"""Helpers for GPU parity tests: move tensors to float64 numpy, compare with the
+stated tolerances, and lay global tensors out into rings with the LIBRARY's
+positions (the oracle always uses its own positions for the reference)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+# Tolerances.
+#   fp32 inputs: norm-wise relative 1e-4 on out and lse (and gradients).
+#   bf16 inputs: 2e-2 max-abs on out, 1e-3 max-abs on lse; gradients
+#   2e-2 * max(1, max|ref|) (bf16 P and dS inside the kernels).
+F32_REL = 1e-4
+BF16_OUT_ABS = 2e-2
+BF16_LSE_ABS = 1e-3
+BF16_GRAD_REL = 2e-2
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a visible GPU")
+    return torch.device("cuda:0")
+
+
+def f64(t) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def _finite_match(got, ref, what):
+    gi, ri = ~np.isfinite(got), ~np.isfinite(ref)
+    assert np.array_equal(gi, ri), f"{what}: non-finite pattern differs ({gi.sum()} vs {ri.sum()})"
+    if gi.any():
+        assert np.array_equal(got[gi], ref[gi]), f"{what}: infinities differ"
+    return ~ri
+
+
+def check_out(got, ref, dtype_is_bf16: bool, what="out"):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    m = _finite_match(got, ref, what)
+    if not m.any():
+        return 0.0
+    err = float(np.max(np.abs(got[m] - ref[m])))
+    if dtype_is_bf16:
+        tol = BF16_OUT_ABS
+    else:
+        tol = F32_REL * max(float(np.max(np.abs(ref[m]))), 1e-30)
+    assert err <= tol, f"{what}: max abs err {err:.3e} > tol {tol:.3e}"
+    return err
+
+
+def check_lse(got, ref, dtype_is_bf16: bool, what="lse"):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    m = _finite_match(got, ref, what)
+    if not m.any():
+        return 0.0
+    err = float(np.max(np.abs(got[m] - ref[m])))
+    tol = BF16_LSE_ABS if dtype_is_bf16 else F32_REL * max(float(np.max(np.abs(ref[m]))), 1e-30)
+    assert err <= tol, f"{what}: max abs err {err:.3e} > tol {tol:.3e}"
+    return err
+
+
+def check_grad(got, ref, dtype_is_bf16: bool, what="grad"):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    mx = float(np.max(np.abs(ref))) if ref.size else 0.0
+    tol = BF16_GRAD_REL * max(1.0, mx) if dtype_is_bf16 else F32_REL * max(mx, 1e-30)
+    assert err <= tol, f"{what}: max abs err {err:.3e} > tol {tol:.3e} (max|ref| {mx:.3e})"
+    return err
+
+
+def ring_from_global(x, layout: str, world: int):
+    """[b, S, h, d] -> [world, b, S/world, h, d] using the library's positions."""
+    import torch
+    import exact_long_context_ra_amd as ra
+    S = x.shape[1]
+    idx = [torch.from_numpy(ra.layout_positions(layout, S, world, r)).to(x.device) for r in range(world)]
+    return torch.stack([x.index_select(1, i) for i in idx]).contiguous(), idx

@@ -1,0 +1,162 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, lays tokens out exactly as the oracle does, and rejects bad
+arguments with the right status before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle_pins import closed_form_pairs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+
+@pytest.fixture(scope="module")
+def ra():
+    import exact_long_context_ra_amd as pkg
+    pkg.lib()
+    return pkg
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(ra):
+    names = _declared_functions()
+    assert len(names) >= 15
+    lib = ra.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_abi_version_and_strings(ra):
+    lib = ra.lib()
+    assert lib.ra_abi_version() == 1
+    assert lib.ra_status_str(0) == b"RA_OK"
+    assert lib.ra_status_str(4) == b"RA_ERR_WORKSPACE"
+    assert lib.ra_kernel_name(0) == b"block_fwd"
+    assert lib.ra_kernel_name(1) == b"block_bwd"
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
+@pytest.mark.parametrize("S,N", [(16, 1), (64, 4), (96, 3), (512, 8), (131072, 8)])
+def test_positions_match_oracle(ra, layout, S, N):
+    for r in range(N):
+        got = ra.layout_positions(layout, S, N, r)
+        want = oracle.layout_positions(layout, S, N, r)
+        assert np.array_equal(got, want), (layout, S, N, r)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
+def test_posmap_segments(ra, layout):
+    S, N = 4096, 8
+    for r in range(N):
+        m = ra.layout_posmap(layout, S, N, r)
+        pos = []
+        for i in range(m.nseg):
+            s = m.seg[i]
+            pos.extend(s.begin + s.stride * np.arange(s.len))
+        assert np.array_equal(np.array(pos), oracle.layout_positions(layout, S, N, r))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
+def test_pair_counts_from_library_positions(ra, layout):
+    """The benchmark's FLOP accounting counts pairs from library positions; the
+    counts must equal the closed forms."""
+    S, N = 256, 8
+    for r in range(N):
+        qpos = ra.layout_positions(layout, S, N, r)
+        got = sum(int(np.searchsorted(np.sort(ra.layout_positions(layout, S, N, s)), qpos, side="right").sum())
+                  for s in range(N))
+        assert got == closed_form_pairs(layout, S, N, r)
+
+
+def _problem(ra, **kw):
+    from exact_long_context_ra_amd._lib import ra_problem
+    p = ra_problem()
+    p.batch, p.heads, p.head_dim, p.dtype = 1, 2, 64, 1
+    p.softmax_scale, p.causal, p.seq_len = 0.0, 1, 64
+    p.cu_seqlens, p.cu_seqlens_host, p.num_seqs = None, None, 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _t(ptr=4096, sb=64 * 2 * 64, st=2 * 64, sh=64):
+    from exact_long_context_ra_amd._lib import ra_tensor
+    return ra_tensor(ptr, sb, st, sh)
+
+
+def _ring_fwd(ra, p, layout=0, world=4, rank=0, q=None, out=None, lse=4096, srank=16 * 128 * 64):
+    lib = ra.lib()
+    return lib.ra_ring_fwd(C.byref(p), layout, world, rank, q or _t(), _t(), _t(), srank, out or _t(),
+                           lse, _t(ptr=None), None)
+
+
+def test_validation_errors(ra):
+    from exact_long_context_ra_amd._lib import RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED
+    lib = ra.lib()
+    assert _ring_fwd(ra, _problem(ra, head_dim=96)) == RA_ERR_UNSUPPORTED
+    assert b"head_dim" in lib.ra_last_error()
+    assert _ring_fwd(ra, _problem(ra), rank=4) == RA_ERR_INVALID_ARG
+    assert _ring_fwd(ra, _problem(ra), layout=7) == RA_ERR_INVALID_ARG
+    assert _ring_fwd(ra, _problem(ra, seq_len=66)) == RA_ERR_INVALID_ARG       # 66 % 4 != 0
+    assert _ring_fwd(ra, _problem(ra, seq_len=68), layout=1) == RA_ERR_INVALID_ARG  # 68 % 8 != 0
+    assert _ring_fwd(ra, _problem(ra), q=_t(ptr=4098)) == RA_ERR_INVALID_ARG  # misaligned
+    assert _ring_fwd(ra, _problem(ra), q=_t(st=2 * 64 + 1)) == RA_ERR_INVALID_ARG
+    assert _ring_fwd(ra, _problem(ra), lse=None) == RA_ERR_INVALID_ARG
+    assert _ring_fwd(ra, _problem(ra, batch=0)) == RA_ERR_INVALID_ARG
+    assert _ring_fwd(ra, _problem(ra, dtype=5)) == RA_ERR_INVALID_ARG
+    # varlen: device pointer required, batch 1, host copy validated
+    cu_bad = (C.c_int32 * 3)(0, 40, 60)  # does not end at seq_len=64
+    p = _problem(ra, num_seqs=2, cu_seqlens=4096, cu_seqlens_host=C.cast(cu_bad, C.c_void_p))
+    assert _ring_fwd(ra, p) == RA_ERR_INVALID_ARG
+    assert b"cu_seqlens" in lib.ra_last_error()
+    cu_dec = (C.c_int32 * 3)(0, 40, 30)
+    p = _problem(ra, num_seqs=2, cu_seqlens=4096, cu_seqlens_host=C.cast(cu_dec, C.c_void_p))
+    assert _ring_fwd(ra, p) == RA_ERR_INVALID_ARG
+    p = _problem(ra, num_seqs=2, cu_seqlens=None)
+    assert _ring_fwd(ra, p) == RA_ERR_INVALID_ARG
+    p = _problem(ra, num_seqs=1, cu_seqlens=4096, batch=2)
+    assert _ring_fwd(ra, p) == RA_ERR_INVALID_ARG
+
+
+def test_block_posmap_validation(ra):
+    from exact_long_context_ra_amd._lib import RA_ERR_INVALID_ARG
+    lib = ra.lib()
+    p = _problem(ra)
+    good = ra.posmap([(0, 1, 16)])
+    dec = ra.posmap([(32, 1, 8), (0, 1, 8)])      # not increasing
+    longm = ra.posmap([(60, 1, 16)])              # runs past seq_len
+    short = ra.posmap([(0, 1, 15)])               # lengths do not sum to lq
+    for bad in (dec, longm, short):
+        st = lib.ra_block_attn_fwd(C.byref(p), _t(), 16, bad, _t(), _t(), 16, good, _t(), 4096, None)
+        assert st == RA_ERR_INVALID_ARG
+        st = lib.ra_block_attn_fwd(C.byref(p), _t(), 16, good, _t(), _t(), 16, bad, _t(), 4096, None)
+        assert st == RA_ERR_INVALID_ARG
+
+
+def test_workspace_validation(ra):
+    from exact_long_context_ra_amd._lib import RA_ERR_WORKSPACE
+    lib = ra.lib()
+    p = _problem(ra)
+    need = lib.ra_ring_workspace_bytes(C.byref(p), 0, 4)
+    assert need == 256  # batch*heads*L*4 = 1*2*16*4 = 128, rounded up to 256
+    st = lib.ra_ring_bwd(C.byref(p), 0, 4, 0, _t(), _t(), _t(), 0, _t(), 4096, _t(), _t(), _t(), _t(), 0,
+                         4096, need - 1, None)
+    assert st == RA_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import exact_long_context_ra_amd._lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libra.so"))
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        L.lib()

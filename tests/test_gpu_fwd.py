@@ -1,0 +1,164 @@
+"""Forward parity: the HIP block step, lse merge and virtual-ring forward
+against the float64 oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check_lse, check_out, dev, f64, log, ring_from_global
+
+pytestmark = pytest.mark.gpu
+
+
+def _ra():
+    import exact_long_context_ra_amd as ra
+    return ra
+
+
+def _dtype(name):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def _segs_positions(segs):
+    return np.concatenate([b + s * np.arange(n) for b, s, n in segs]).astype(np.int64)
+
+
+BLOCK_CASES = [
+    # (name, q segments, k segments, seq_len, causal, cu_seqlens)
+    ("contig_diag", [(0, 1, 256)], [(0, 1, 256)], 256, True, None),
+    ("contig_ragged_past", [(300, 1, 200)], [(0, 1, 150)], 600, True, None),
+    ("ragged_noncausal", [(0, 1, 77)], [(100, 1, 131)], 300, False, None),
+    ("zigzag_two_seg", [(64, 1, 64), (448, 1, 64)], [(0, 1, 64), (512, 1, 64)], 576, True, None),
+    ("zigzag_ragged", [(40, 1, 40), (400, 1, 40)], [(80, 1, 40), (360, 1, 40)], 440, True, None),
+    ("stripe_src_le_r", [(3, 8, 160)], [(1, 8, 160)], 1280, True, None),
+    ("stripe_src_gt_r", [(1, 8, 160)], [(3, 8, 160)], 1280, True, None),
+    ("future_block_empty", [(0, 1, 130)], [(200, 1, 70)], 300, True, None),
+    ("varlen_causal", [(0, 1, 300)], [(0, 1, 300)], 300, True, [0, 1, 65, 66, 200, 300]),
+    ("varlen_noncausal", [(0, 1, 300)], [(0, 1, 300)], 300, False, [0, 129, 130, 300]),
+    ("varlen_cross_block", [(150, 1, 150)], [(0, 1, 150)], 300, True, [0, 40, 170, 171, 300]),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=[c[0] for c in BLOCK_CASES])
+def test_block_fwd(case, D, dt):
+    import torch
+    ra = _ra()
+    name, qsegs, ksegs, S, causal, cu = case
+    log(f"block_fwd {name} D={D} {dt}")
+    qpos, kpos = _segs_positions(qsegs), _segs_positions(ksegs)
+    H, B = 2, 2 if cu is None else 1
+    q, k, v = synth.draw_normal([(B, len(qpos), H, D), (B, len(kpos), H, D), (B, len(kpos), H, D)],
+                                _dtype(dt), seed=7, device="cpu")
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    out, lse = ra.block_attn_fwd(q, k, v, ra.posmap(qsegs), ra.posmap(ksegs), seq_len=S, causal=causal,
+                                 cu_seqlens=cu)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), qpos, kpos, causal, cu)
+    bf = dt == "bf16"
+    check_out(f64(out), ro, bf)
+    check_lse(f64(lse), rl, bf)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_lse_merge_standalone(dt):
+    """Block results of a random key split, merged by ra_lse_merge, equal one-shot attention."""
+    import torch
+    ra = _ra()
+    log(f"lse_merge {dt}")
+    S, H, D = 384, 2, 128
+    q, k, v = synth.qkv(S, H, D, _dtype(dt), seed=3, device="cpu")
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    pos = np.arange(S)
+    qm = ra.posmap([(0, 1, S)])
+    out = lse = None
+    # three contiguous key blocks, merged out of order: [256, 384), [0, 100), [100, 256)
+    for a, b in [(256, 384), (0, 100), (100, 256)]:
+        ob, lb = ra.block_attn_fwd(q, k[:, a:b].contiguous(), v[:, a:b].contiguous(), qm,
+                                   ra.posmap([(a, 1, b - a)]), seq_len=S, causal=True)
+        if out is None:
+            out, lse = ob, lb
+        else:
+            ra.lse_merge(out, lse, ob, lb)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), pos, pos, True)
+    check_out(f64(out), ro, dt == "bf16")
+    check_lse(f64(lse), rl, dt == "bf16")
+
+
+RING_CASES = [
+    # (layout, S, N, H, D, dtype, causal, cu_seqlens, batch)
+    ("contiguous", 512, 4, 2, 64, "f32", False, None, 1),     # tiny virtual ring (seed 0)
+    ("contiguous", 1024, 4, 2, 128, "f32", True, None, 1),
+    ("zigzag", 1024, 4, 2, 128, "f32", True, None, 1),
+    ("stripe", 1024, 4, 2, 128, "f32", True, None, 1),
+    ("contiguous", 1024, 4, 2, 128, "bf16", True, None, 2),
+    ("zigzag", 2048, 4, 2, 128, "bf16", True, None, 1),
+    ("stripe", 2048, 8, 2, 128, "bf16", True, None, 1),
+    ("zigzag", 800, 4, 2, 64, "bf16", True, None, 1),         # chunks of 100: ragged tiles
+    ("stripe", 1608, 8, 2, 64, "f32", True, None, 1),        # 201 rows per rank
+    ("contiguous", 1600, 8, 2, 128, "bf16", False, None, 1),
+    ("contiguous", 1024, 1, 2, 128, "bf16", True, None, 1),   # N = 1: plain attention
+    ("contiguous", 1536, 4, 2, 128, "bf16", True, "varlen", 1),
+    ("zigzag", 1536, 4, 2, 128, "f32", True, "varlen", 1),
+    ("stripe", 1536, 4, 2, 64, "bf16", True, "varlen", 1),
+]
+
+
+def _varlen_cu(S):
+    # 1-token sequences, a tile-straddling run and a long tail
+    lengths = [1, 63, 1, 130, 257, 1]
+    lengths.append(S - sum(lengths))
+    return synth.cu_seqlens(lengths)
+
+
+@pytest.mark.parametrize("case", RING_CASES, ids=lambda c: "-".join(str(x) for x in c))
+def test_ring_fwd(case):
+    import torch
+    ra = _ra()
+    layout, S, N, H, D, dt, causal, cu, B = case
+    log(f"ring_fwd {case}")
+    cu = _varlen_cu(S) if cu == "varlen" else None
+    seed = 0 if S == 512 else 11
+    q, k, v = synth.qkv(S, H, D, _dtype(dt), seed=seed, device="cpu", batch=B)
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    kr, idx = ring_from_global(k, layout, N)
+    vr, _ = ring_from_global(v, layout, N)
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    allk = np.arange(S)
+    bf = dt == "bf16"
+    for r in range(N):
+        ql = q.index_select(1, idx[r]).contiguous()
+        out, lse, lowp = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=causal, cu_seqlens=cu, want_lowp=True)
+        torch.cuda.synchronize()
+        opos = oracle.layout_positions(layout, S, N, r)
+        assert np.array_equal(opos, idx[r].cpu().numpy())
+        ro, rl = oracle.attention(q64[:, opos], k64, v64, opos, allk, causal, cu)
+        check_out(f64(out), ro, bf, what=f"out r={r}")
+        check_lse(f64(lse), rl, bf, what=f"lse r={r}")
+        check_out(f64(lowp), ro, bf, what=f"out_lowp r={r}")
+
+
+def test_ring_fwd_deterministic_and_teeth():
+    """Two runs are bitwise identical; and dropping a ring step in the oracle
+    breaks parity (the comparison has teeth)."""
+    import torch
+    ra = _ra()
+    log("ring_fwd determinism")
+    layout, S, N, H, D = "zigzag", 1024, 4, 2, 128
+    q, k, v = synth.qkv(S, H, D, torch.bfloat16, seed=5, device="cpu")
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    kr, idx = ring_from_global(k, layout, N)
+    vr, _ = ring_from_global(v, layout, N)
+    r = 2
+    ql = q.index_select(1, idx[r]).contiguous()
+    o1, l1, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True)
+    o2, l2, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    kr64, vr64 = oracle.to_ring(f64(k), layout, N), oracle.to_ring(f64(v), layout, N)
+    dropped = oracle.ring_forward(layout, N, r, f64(ql), kr64, vr64, True, steps=[0, 1, 3])
+    with pytest.raises(AssertionError):
+        check_out(f64(o1), dropped[0], True)
