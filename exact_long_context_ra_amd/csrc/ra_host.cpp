@@ -115,7 +115,10 @@ ra_status check_tensor(const char* name, const ra_tensor& t, size_t esz, int64_t
   const int64_t b16 = 16 / (int64_t)esz;  // elements per 16 bytes
   RA_CHECK(t.stride_b % b16 == 0 && t.stride_t % b16 == 0 && t.stride_h % b16 == 0, RA_ERR_INVALID_ARG,
            "%s: strides must keep rows 16-byte aligned", name);
-  (void)rows;
+  // Kernels address one (batch, head) slice with 32-bit byte offsets and read
+  // up to 256 rows past its end (those reads return zeros).
+  RA_CHECK((rows + 256) * t.stride_t * (int64_t)esz + 512 * (int64_t)esz < (int64_t(1) << 31), RA_ERR_UNSUPPORTED,
+           "%s: a (batch, head) slice spans more than 2 GiB", name);
   return RA_OK;
 }
 

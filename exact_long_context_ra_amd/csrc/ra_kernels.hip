@@ -155,90 +155,112 @@ __device__ __forceinline__ int xcd_logical(int bid, int total) {
 }
 
 // ============================================================================================
+// Buffer loads.  Each (batch, head) slice of a tensor gets a range-checked
+// buffer descriptor; a read past the slice returns zeros, so ragged tiles need
+// neither branches nor clamped addresses (and the loads of a tile can all be
+// in flight at once).
+// ============================================================================================
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ f32x4 bload16f(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float bload4f(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ uint16_t bload2(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+// Bytes spanned by `rows` rows of `dim` elements at a stride of `st` elements.
+__device__ __forceinline__ uint32_t slice_bytes(int rows, int64_t st, int esz, int dim) {
+  return rows <= 0 ? 0u : (uint32_t)((int64_t)(rows - 1) * st * esz + (int64_t)dim * esz);
+}
+
+// ============================================================================================
 // Forward
 // ============================================================================================
 
-constexpr int FBK = 64;  // keys per forward tile
+constexpr int FBK = 64;             // keys per forward tile
+constexpr float RESCALE_TH = 8.f;   // rescale O only when a row max grows by more than 2^8
 
 template <int D, bool BF16>
 struct FwdCfg {
-  // bf16: K rows padded by 16 bytes; V^T rows of 64 keys, swizzled.
-  // fp32: K rows padded by 2 floats, V rows padded by 4 floats (natural layout).
+  // bf16: K rows padded by 16 bytes; V^T rows of 64 keys, swizzled; two buffers.
+  // fp32: K rows padded by 2 floats, V rows padded by 4 floats; one buffer.
   static constexpr int KSTR = BF16 ? (D + 8) * 2 : (D + 2) * 4;
   static constexpr int VSZ = BF16 ? D * 128 : FBK * (D + 4) * 4;
   static constexpr int VSTR = (D + 4) * 4;  // fp32 V row stride
-  static constexpr int LDS = FBK * KSTR + VSZ;
+  static constexpr int BUF = FBK * KSTR + VSZ;
+  static constexpr int NBUF = BF16 ? 2 : 1;
+  static constexpr int LDS = NBUF * BUF;
 };
 
+// bf16 K/V tile: global -> registers (issued one tile ahead) -> LDS.
 template <int D>
-__device__ __forceinline__ void fwd_stage_bf16(const uint16_t* kb, int64_t kst, const uint16_t* vb, int64_t vst,
-                                               int j0, int lk, char* sK, char* sV, int tid) {
-  using C = FwdCfg<D, true>;
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int RPP = NT / CPR;     // K rows per pass
-  constexpr int KP = FBK / RPP;     // K passes
-  constexpr int VITEMS = (FBK / 4) * CPR;
-  constexpr int VP = (VITEMS + NT - 1) / NT;
-  u32x4 kr[KP];
+struct KVStageBf16 {
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int RPP = NT / CPR;  // K rows per pass
+  static constexpr int KP = FBK / RPP;  // K passes
+  static constexpr int VITEMS = (FBK / 4) * CPR;  // (4 keys x 8 d) items of V
+  u32x4 k[KP];
+  u32x4 v[4];
+
+  __device__ __forceinline__ void load(Rsrc rk, Rsrc rv, uint32_t kst, uint32_t vst, int j0, int tid) {
 #pragma unroll
-  for (int p = 0; p < KP; ++p) {
-    int r = p * RPP + tid / CPR, c = tid % CPR, j = j0 + r;
-    kr[p] = u32x4{0u, 0u, 0u, 0u};
-    if (j < lk) kr[p] = *reinterpret_cast<const u32x4*>(kb + (int64_t)j * kst + c * 8);
-  }
-  u32x4 vr[VP][4];
+    for (int p = 0; p < KP; ++p) {
+      const int r = p * RPP + tid / CPR, c = tid % CPR;
+      k[p] = bload16(rk, (uint32_t)(j0 + r) * kst + c * 16);
+    }
+    if (tid < VITEMS) {
+      const int c = tid % CPR, kq = tid / CPR;
 #pragma unroll
-  for (int p = 0; p < VP; ++p) {
-    int it = p * NT + tid;
-    int c = it % CPR, kq = it / CPR;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int j = j0 + 4 * kq + i;
-      vr[p][i] = u32x4{0u, 0u, 0u, 0u};
-      if (it < VITEMS && j < lk) vr[p][i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)j * vst + c * 8);
+      for (int i = 0; i < 4; ++i) v[i] = bload16(rv, (uint32_t)(j0 + 4 * kq + i) * vst + c * 16);
     }
   }
+  __device__ __forceinline__ void store(char* sK, char* sV, int tid) const {
+    constexpr int KSTR = FwdCfg<D, true>::KSTR;
 #pragma unroll
-  for (int p = 0; p < KP; ++p) {
-    int r = p * RPP + tid / CPR, c = tid % CPR;
-    *reinterpret_cast<u32x4*>(sK + r * C::KSTR + c * 16) = kr[p];
-  }
-#pragma unroll
-  for (int p = 0; p < VP; ++p) {
-    int it = p * NT + tid;
-    if (it < VITEMS) {
-      int c = it % CPR, kq = it / CPR;
+    for (int p = 0; p < KP; ++p) {
+      const int r = p * RPP + tid / CPR, c = tid % CPR;
+      *reinterpret_cast<u32x4*>(sK + r * KSTR + c * 16) = k[p];
+    }
+    if (tid < VITEMS) {
+      const int c = tid % CPR, kq = tid / CPR;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        int e = dd >> 1;
-        uint32_t x0 = vr[p][0][e], x1 = vr[p][1][e], x2 = vr[p][2][e], x3 = vr[p][3][e];
+        const int e = dd >> 1;
         uint32_t w0, w1;
         if (dd & 1) {
-          w0 = (x0 >> 16) | (x1 & 0xffff0000u);
-          w1 = (x2 >> 16) | (x3 & 0xffff0000u);
+          w0 = (v[0][e] >> 16) | (v[1][e] & 0xffff0000u);
+          w1 = (v[2][e] >> 16) | (v[3][e] & 0xffff0000u);
         } else {
-          w0 = (x0 & 0xffffu) | (x1 << 16);
-          w1 = (x2 & 0xffffu) | (x3 << 16);
+          w0 = (v[0][e] & 0xffffu) | (v[1][e] << 16);
+          w1 = (v[2][e] & 0xffffu) | (v[3][e] << 16);
         }
         *reinterpret_cast<u32x2*>(sV + tr_off(8 * c + dd, 4 * kq)) = u32x2{w0, w1};
       }
     }
   }
-}
+};
 
 template <int D>
-__device__ __forceinline__ void fwd_stage_f32(const float* kb, int64_t kst, const float* vb, int64_t vst,
-                                              int j0, int lk, char* sK, char* sV, int tid) {
+__device__ __forceinline__ void fwd_stage_f32(Rsrc rk, Rsrc rv, uint32_t kst, uint32_t vst, int j0, char* sK,
+                                              char* sV, int tid) {
   using C = FwdCfg<D, false>;
   constexpr int CPR = D / 4;  // float4 chunks per row
   constexpr int ITEMS = FBK * CPR;
+#pragma unroll 4
   for (int it = tid; it < ITEMS; it += NT) {
-    int r = it / CPR, c = it % CPR, j = j0 + r;
-    f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-    if (j < lk) {
-      kv = *reinterpret_cast<const f32x4*>(kb + (int64_t)j * kst + c * 4);
-      vv = *reinterpret_cast<const f32x4*>(vb + (int64_t)j * vst + c * 4);
-    }
+    const int r = it / CPR, c = it % CPR;
+    const f32x4 kv = bload16f(rk, (uint32_t)(j0 + r) * kst + c * 16);
+    const f32x4 vv = bload16f(rv, (uint32_t)(j0 + r) * vst + c * 16);
     float* kd = reinterpret_cast<float*>(sK + r * C::KSTR) + c * 4;
     *reinterpret_cast<float2*>(kd) = make_float2(kv[0], kv[1]);
     *reinterpret_cast<float2*>(kd + 2) = make_float2(kv[2], kv[3]);
@@ -246,13 +268,108 @@ __device__ __forceinline__ void fwd_stage_f32(const float* kb, int64_t kst, cons
   }
 }
 
+// One 64-key tile for one wave (32 query rows): S^T, mask, online softmax, O^T += V^T P^T.
+template <int D, bool BF16, typename QF>
+__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int j0, const char* sK, const char* sV, const QF* qf,
+                                         const Bounds& rb, const Bounds& wv_f, const Bounds& wv_l,
+                                         bool wave_has_rows, float& m_run, float& l_run, f32x16* o, int l32,
+                                         int hf) {
+  using C = FwdCfg<D, BF16>;
+  constexpr int NDB = D / 32;
+  const int jl = min(a.lk, j0 + FBK) - 1;
+  const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
+  if (!wave_has_rows || kmax < wv_f.lo || kmin > wv_l.hi) return;  // nothing visible to this wave
+  const bool wave_full = (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
+  const float sl2 = a.scale_log2;
+
+  f32x16 st[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    f32x16 acc = f32x16{};
+    if constexpr (BF16) {
+      const char* kr = sK + (c2 * 32 + row_perm(l32)) * C::KSTR + hf * 16;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(kr + c * 32), qf[c], acc);
+    } else {
+      const float* kr = reinterpret_cast<const float*>(sK + (c2 * 32 + row_perm(l32)) * C::KSTR) + hf;
+#pragma unroll
+      for (int t = 0; t < D / 2; ++t) acc = mfma_f32(kr[2 * t], qf[t], acc);
+    }
+    st[c2] = acc;
+  }
+  if (!wave_full) {
+    const bool in0 = j0 < a.kmap.s0.len;
+    const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
+    const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = j0 + c2 * 32 + reg_row(v, hf);
+        const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
+        const bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+        st[c2][v] = ok ? st[c2][v] : NEG_INF;
+      }
+  }
+  float mx = NEG_INF;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  // Lazy rescale: the running max only moves when a row max exceeds it by
+  // more than RESCALE_TH (so P <= 2^RESCALE_TH); the result is exact either way.
+  const bool grow = mx > m_run + RESCALE_TH;
+  if (__any(grow)) {
+    const float m_new = grow ? mx : m_run;
+    const float alpha = (m_new == m_run) ? 1.f : ex2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+  float rs = 0.f;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = ex2(__builtin_fmaf(st[c2][v], sl2, -m_use));
+      st[c2][v] = p;
+      rs += p;
+    }
+  l_run += rs;
+
+  // O^T += V^T P^T
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
+        const int kcol = c2 * 32 + 16 * u + 8 * hf;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[d] = mfma_bf16(ld_bf16x8(sV + tr_off(d * 32 + l32, kcol)), pb, o[d]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float* vr = reinterpret_cast<const float*>(sV + (c2 * 32 + reg_row(t, hf)) * C::VSTR) + l32;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) o[d] = mfma_f32(vr[d * 32], st[c2][t], o[d]);
+      }
+    }
+  }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D, BF16>;
-  constexpr int NDB = D / 32;  // 32-wide d blocks of the output
+  constexpr int NDB = D / 32;
+  constexpr int ESZ = BF16 ? 2 : 4;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* sK = smem;
-  char* sV = smem + FBK * C::KSTR;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
@@ -268,10 +385,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   const int row = w_first + l32;
   const bool row_ok = row <= r_last;
 
-  using TI = typename std::conditional<BF16, uint16_t, float>::type;
-  const TI* qb = reinterpret_cast<const TI*>(a.q.ptr) + b * a.q.sb + head * a.q.sh;
-  const TI* kb = reinterpret_cast<const TI*>(a.k.ptr) + b * a.k.sb + head * a.k.sh;
-  const TI* vb = reinterpret_cast<const TI*>(a.v.ptr) + b * a.v.sb + head * a.v.sh;
+  const char* qbase = reinterpret_cast<const char*>(a.q.ptr) + (b * a.q.sb + head * a.q.sh) * ESZ;
+  const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * ESZ;
+  const char* vbase = reinterpret_cast<const char*>(a.v.ptr) + (b * a.v.sb + head * a.v.sh) * ESZ;
+  const Rsrc rq = make_rsrc(qbase, slice_bytes(a.lq, a.q.st, ESZ, D));
+  const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, ESZ, D));
+  const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, ESZ, D));
+  const uint32_t qst = (uint32_t)(a.q.st * ESZ), kst = (uint32_t)(a.k.st * ESZ), vst = (uint32_t)(a.v.st * ESZ);
 
   // Query fragments (B operand of S^T = K Q^T), kept in registers.
   constexpr int NQF = BF16 ? D / 16 : D / 2;
@@ -280,12 +400,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   if constexpr (BF16) {
 #pragma unroll
     for (int c = 0; c < NQF; ++c)
-      qf[c] = row_ok ? ld_bf16x8(qb + (int64_t)row * a.q.st + 16 * c + 8 * hf) : zero_bf16x8();
+      qf[c] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)row * qst + (16 * c + 8 * hf) * 2));
   } else {
 #pragma unroll
     for (int c4 = 0; c4 < D / 4; ++c4) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) x = *reinterpret_cast<const f32x4*>(qb + (int64_t)row * a.q.st + 4 * c4);
+      const f32x4 x = bload16f(rq, (uint32_t)row * qst + 16 * c4);
       qf[2 * c4] = hf ? x[1] : x[0];
       qf[2 * c4 + 1] = hf ? x[3] : x[2];
     }
@@ -305,100 +424,37 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   f32x16 o[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) o[d] = f32x16{};
-  const float sl2 = a.scale_log2;
 
   if (kbeg < kend) {
     const int jt0 = kbeg / FBK, jt1 = (kend - 1) / FBK;
-    for (int jt = jt0; jt <= jt1; ++jt) {
-      const int j0 = jt * FBK;
-      if constexpr (BF16)
-        fwd_stage_bf16<D>(kb, a.k.st, vb, a.v.st, j0, a.lk, sK, sV, tid);
-      else
-        fwd_stage_f32<D>(kb, a.k.st, vb, a.v.st, j0, a.lk, sK, sV, tid);
+    if constexpr (BF16) {
+      // Software pipeline: tile jt+1 is fetched into registers while tile jt is
+      // computed from LDS, then written to the other LDS buffer.
+      KVStageBf16<D> stage;
+      stage.load(rk, rv, kst, vst, jt0 * FBK, tid);
+      stage.store(smem, smem + FBK * C::KSTR, tid);
       __syncthreads();
-
-      const int jl = min(a.lk, j0 + FBK) - 1;
-      const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
-      const bool wave_empty = !wave_has_rows || kmax < wv_f.lo || kmin > wv_l.hi;
-      const bool wave_full = (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
-
-      if (!wave_empty) {
-        // S^T for two 32-key chunks.
-        f32x16 st[2];
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          f32x16 acc = f32x16{};
-          if constexpr (BF16) {
-            const char* kr = sK + (c2 * 32 + row_perm(l32)) * C::KSTR + hf * 16;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(kr + c * 32), qf[c], acc);
-          } else {
-            const float* kr = reinterpret_cast<const float*>(sK + (c2 * 32 + row_perm(l32)) * C::KSTR) + hf;
-#pragma unroll
-            for (int t = 0; t < D / 2; ++t) acc = mfma_f32(kr[2 * t], qf[t], acc);
-          }
-          st[c2] = acc;
+      for (int jt = jt0; jt <= jt1; ++jt) {
+        const int cur = (jt - jt0) & 1;
+        const char* sK = smem + cur * C::BUF;
+        const bool more = jt < jt1;
+        if (more) stage.load(rk, rv, kst, vst, (jt + 1) * FBK, tid);
+        fwd_tile<D, true>(a, jt * FBK, sK, sK + FBK * C::KSTR, qf, rb, wv_f, wv_l, wave_has_rows, m_run, l_run, o,
+                          l32, hf);
+        if (more) {
+          char* nK = smem + (cur ^ 1) * C::BUF;
+          stage.store(nK, nK + FBK * C::KSTR, tid);
         }
-        if (!wave_full) {
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              int j = j0 + c2 * 32 + reg_row(v, hf);
-              int kp = map_pos(a.kmap, min(j, jl));
-              bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
-              st[c2][v] = ok ? st[c2][v] : NEG_INF;
-            }
-          }
-        }
-        // Online softmax in base 2 (scores scaled by softmax_scale*log2(e)).
-        float mx = NEG_INF;
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * sl2);
-        const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-        const float alpha = ex2(m_run - m_use);
-        float rs = 0.f;
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float p = ex2(__builtin_fmaf(st[c2][v], sl2, -m_use));
-            st[c2][v] = p;
-            rs += p;
-          }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) o[d] *= alpha;
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          if constexpr (BF16) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              bf16x8 pb;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
-              const int kcol = c2 * 32 + 16 * u + 8 * hf;
-#pragma unroll
-              for (int d = 0; d < NDB; ++d) o[d] = mfma_bf16(ld_bf16x8(sV + tr_off(d * 32 + l32, kcol)), pb, o[d]);
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-              const float* vr = reinterpret_cast<const float*>(sV + (c2 * 32 + reg_row(t, hf)) * C::VSTR) + l32;
-#pragma unroll
-              for (int d = 0; d < NDB; ++d) o[d] = mfma_f32(vr[d * 32], st[c2][t], o[d]);
-            }
-          }
-        }
+        __syncthreads();
       }
-      __syncthreads();
+    } else {
+      for (int jt = jt0; jt <= jt1; ++jt) {
+        fwd_stage_f32<D>(rk, rv, kst, vst, jt * FBK, smem, smem + FBK * C::KSTR, tid);
+        __syncthreads();
+        fwd_tile<D, false>(a, jt * FBK, smem, smem + FBK * C::KSTR, qf, rb, wv_f, wv_l, wave_has_rows, m_run,
+                           l_run, o, l32, hf);
+        __syncthreads();
+      }
     }
   }
 
@@ -420,7 +476,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const float lse_old = *lse_p;
     const float mm = fmaxf(lse_old, lse_b);
     if (mm == NEG_INF) {
-      wa = 0.f; wb = 0.f; lse_new = NEG_INF;
+      wa = 0.f;
+      wb = 0.f;
+      lse_new = NEG_INF;
     } else {
       const float ea = expf(lse_old - mm), eb = expf(lse_b - mm);
       const float s = ea + eb;
@@ -429,6 +487,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
       wb = eb / s * inv;
     }
   }
+  using TI = typename std::conditional<BF16, uint16_t, float>::type;
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
 #pragma unroll
@@ -436,7 +495,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
       const int d0 = d * 32 + 8 * g + 4 * hf;
       f32x4 val = {o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb};
       if (a.mode == FWD_MERGE) {
-        f32x4 old = *reinterpret_cast<const f32x4*>(orow + d0);
+        const f32x4 old = *reinterpret_cast<const f32x4*>(orow + d0);
         val += wa * old;
       }
       *reinterpret_cast<f32x4*>(orow + d0) = val;
@@ -444,9 +503,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
         TI* lp = reinterpret_cast<TI*>(a.out_lowp.ptr) + b * a.out_lowp.sb + (int64_t)row * a.out_lowp.st +
                  head * a.out_lowp.sh + d0;
         if constexpr (BF16) {
-          __bf16 t0 = (__bf16)val[0], t1 = (__bf16)val[1], t2 = (__bf16)val[2], t3 = (__bf16)val[3];
-          uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, t0) | ((uint32_t)__builtin_bit_cast(uint16_t, t1) << 16);
-          uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, t2) | ((uint32_t)__builtin_bit_cast(uint16_t, t3) << 16);
+          const __bf16 t0 = (__bf16)val[0], t1 = (__bf16)val[1], t2 = (__bf16)val[2], t3 = (__bf16)val[3];
+          const uint32_t p0 =
+              (uint32_t)__builtin_bit_cast(uint16_t, t0) | ((uint32_t)__builtin_bit_cast(uint16_t, t1) << 16);
+          const uint32_t p1 =
+              (uint32_t)__builtin_bit_cast(uint16_t, t2) | ((uint32_t)__builtin_bit_cast(uint16_t, t3) << 16);
           *reinterpret_cast<u32x2*>(lp) = u32x2{p0, p1};
         } else {
           *reinterpret_cast<f32x4*>(lp) = val;
@@ -468,39 +529,83 @@ struct BwdCfg {
   static constexpr int QSTR = BF16 ? (D + 8) * 2 : (D + 2) * 4;  // natural Q / dO rows
   static constexpr int QTSZ = BF16 ? D * 128 : 0;                // transposed Q / dO tiles
   static constexpr int SSTR = BF16 ? (BWD_BK + 8) * 2 : (BWD_BK + 2) * 4;  // dS rows
+  // one buffer: Q, Q^T, dO, dO^T, then lse*log2e, delta, row lo, row hi
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_QT = OFF_Q + BQB * QSTR;
   static constexpr int OFF_DO = OFF_QT + QTSZ;
   static constexpr int OFF_DOT = OFF_DO + BQB * QSTR;
-  static constexpr int OFF_DS = OFF_DOT + QTSZ;
-  static constexpr int OFF_LSE = OFF_DS + BQB * SSTR;
+  static constexpr int OFF_LSE = OFF_DOT + QTSZ;
   static constexpr int OFF_DEL = OFF_LSE + BQB * 4;
   static constexpr int OFF_LO = OFF_DEL + BQB * 4;
   static constexpr int OFF_HI = OFF_LO + BQB * 4;
-  static constexpr int LDS = OFF_HI + BQB * 4;
+  static constexpr int BUF = OFF_HI + BQB * 4;
+  static constexpr int NBUF = BF16 ? 2 : 1;
+  static constexpr int OFF_DS = NBUF * BUF;
+  static constexpr int LDS = OFF_DS + BQB * SSTR;
 };
 
-// Stage a 64-row tile of a [rows][D] bf16 tensor into LDS, natural and transposed.
-template <int D>
-__device__ __forceinline__ void bwd_stage_bf16(const uint16_t* src, int64_t st, int r0, int lq, char* sN, char* sT,
-                                               int tid) {
-  using C = BwdCfg<D, true>;
-  constexpr int CPR = D / 8;
-  constexpr int ITEMS = (BQB / 4) * CPR;
-  for (int it = tid; it < ITEMS; it += NT) {
-    int c = it % CPR, rq = it / CPR;
-    u32x4 x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int r = r0 + 4 * rq + i;
-      x[i] = u32x4{0u, 0u, 0u, 0u};
-      if (r < lq) x[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * st + c * 8);
+// Per-row data of a query tile: lse (log2 units; +inf for rows without keys or
+// past the end), delta, and the visible key interval.
+struct RowStage {
+  float l, dl;
+  int lo, hi;
+  __device__ __forceinline__ void load(const BwdArgs& a, const float* lse_b, const float* del_b, int r0, int tid) {
+    if (tid < BQB) {
+      const int r = r0 + tid;
+      if (r < a.lq) {
+        const float x = lse_b[r];
+        l = (x == NEG_INF) ? POS_INF : x * LOG2E;
+        dl = del_b[r];
+        const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, r));
+        lo = rb.lo;
+        hi = rb.hi;
+      } else {
+        l = POS_INF;
+        dl = 0.f;
+        lo = INT_BIG;
+        hi = -1;
+      }
     }
+  }
+  template <class C>
+  __device__ __forceinline__ void store(char* buf, int tid) const {
+    if (tid < BQB) {
+      reinterpret_cast<float*>(buf + C::OFF_LSE)[tid] = l;
+      reinterpret_cast<float*>(buf + C::OFF_DEL)[tid] = dl;
+      reinterpret_cast<int*>(buf + C::OFF_LO)[tid] = lo;
+      reinterpret_cast<int*>(buf + C::OFF_HI)[tid] = hi;
+    }
+  }
+};
+
+// bf16 query-tile staging (Q and dO, natural and transposed): global ->
+// registers one tile ahead -> LDS.
+template <int D>
+struct QStageBf16 {
+  static constexpr int CPR = D / 8;
+  static constexpr int ITEMS = (BQB / 4) * CPR;  // (4 rows x 8 d) items
+  u32x4 q[4], g[4];
+  RowStage rows;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, Rsrc rq, Rsrc rdo, uint32_t qst, uint32_t dst,
+                                       const float* lse_b, const float* del_b, int r0, int tid) {
+    if (tid < ITEMS) {
+      const int c = tid % CPR, rq4 = tid / CPR;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sN + (4 * rq + i) * C::QSTR + c * 16) = x[i];
+      for (int i = 0; i < 4; ++i) {
+        q[i] = bload16(rq, (uint32_t)(r0 + 4 * rq4 + i) * qst + c * 16);
+        g[i] = bload16(rdo, (uint32_t)(r0 + 4 * rq4 + i) * dst + c * 16);
+      }
+    }
+    rows.load(a, lse_b, del_b, r0, tid);
+  }
+  __device__ __forceinline__ static void put(const u32x4* x, char* sN, char* sT, int c, int rq4) {
+    constexpr int QSTR = BwdCfg<D, true>::QSTR;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(sN + (4 * rq4 + i) * QSTR + c * 16) = x[i];
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-      int e = dd >> 1;
+      const int e = dd >> 1;
       uint32_t w0, w1;
       if (dd & 1) {
         w0 = (x[0][e] >> 16) | (x[1][e] & 0xffff0000u);
@@ -509,40 +614,50 @@ __device__ __forceinline__ void bwd_stage_bf16(const uint16_t* src, int64_t st, 
         w0 = (x[0][e] & 0xffffu) | (x[1][e] << 16);
         w1 = (x[2][e] & 0xffffu) | (x[3][e] << 16);
       }
-      *reinterpret_cast<u32x2*>(sT + tr_off(8 * c + dd, 4 * rq)) = u32x2{w0, w1};
+      *reinterpret_cast<u32x2*>(sT + tr_off(8 * c + dd, 4 * rq4)) = u32x2{w0, w1};
     }
   }
-}
+  __device__ __forceinline__ void store(char* buf, int tid) const {
+    using C = BwdCfg<D, true>;
+    if (tid < ITEMS) {
+      const int c = tid % CPR, rq4 = tid / CPR;
+      put(q, buf + C::OFF_Q, buf + C::OFF_QT, c, rq4);
+      put(g, buf + C::OFF_DO, buf + C::OFF_DOT, c, rq4);
+    }
+    rows.store<C>(buf, tid);
+  }
+};
 
 template <int D>
-__device__ __forceinline__ void bwd_stage_f32(const float* src, int64_t st, int r0, int lq, char* sN, int tid) {
+__device__ __forceinline__ void bwd_stage_f32(const BwdArgs& a, Rsrc rq, Rsrc rdo, uint32_t qst, uint32_t dst,
+                                              const float* lse_b, const float* del_b, int r0, char* buf, int tid) {
   using C = BwdCfg<D, false>;
   constexpr int CPR = D / 4;
   constexpr int ITEMS = BQB * CPR;
+#pragma unroll 4
   for (int it = tid; it < ITEMS; it += NT) {
-    int r = it / CPR, c = it % CPR;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (r0 + r < lq) x = *reinterpret_cast<const f32x4*>(src + (int64_t)(r0 + r) * st + c * 4);
-    float* d = reinterpret_cast<float*>(sN + r * C::QSTR) + c * 4;
-    *reinterpret_cast<float2*>(d) = make_float2(x[0], x[1]);
-    *reinterpret_cast<float2*>(d + 2) = make_float2(x[2], x[3]);
+    const int r = it / CPR, c = it % CPR;
+    const f32x4 x = bload16f(rq, (uint32_t)(r0 + r) * qst + c * 16);
+    const f32x4 y = bload16f(rdo, (uint32_t)(r0 + r) * dst + c * 16);
+    float* dq = reinterpret_cast<float*>(buf + C::OFF_Q + r * C::QSTR) + c * 4;
+    float* dd = reinterpret_cast<float*>(buf + C::OFF_DO + r * C::QSTR) + c * 4;
+    *reinterpret_cast<float2*>(dq) = make_float2(x[0], x[1]);
+    *reinterpret_cast<float2*>(dq + 2) = make_float2(x[2], x[3]);
+    *reinterpret_cast<float2*>(dd) = make_float2(y[0], y[1]);
+    *reinterpret_cast<float2*>(dd + 2) = make_float2(y[2], y[3]);
   }
+  RowStage rows;
+  rows.load(a, lse_b, del_b, r0, tid);
+  rows.store<C>(buf, tid);
 }
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
   using C = BwdCfg<D, BF16>;
   constexpr int NDB = D / 32;
+  constexpr int ESZ = BF16 ? 2 : 4;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* sQ = smem + C::OFF_Q;
-  char* sQt = smem + C::OFF_QT;
-  char* sDO = smem + C::OFF_DO;
-  char* sDOt = smem + C::OFF_DOT;
   char* sDS = smem + C::OFF_DS;
-  float* sLse = reinterpret_cast<float*>(smem + C::OFF_LSE);
-  float* sDel = reinterpret_cast<float*>(smem + C::OFF_DEL);
-  int* sLo = reinterpret_cast<int*>(smem + C::OFF_LO);
-  int* sHi = reinterpret_cast<int*>(smem + C::OFF_HI);
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
@@ -550,11 +665,16 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
   const int bh = logical / a.n_ktiles;
   const int head = bh % a.heads, b = bh / a.heads;
 
-  using TI = typename std::conditional<BF16, uint16_t, float>::type;
-  const TI* qb = reinterpret_cast<const TI*>(a.q.ptr) + b * a.q.sb + head * a.q.sh;
-  const TI* kb = reinterpret_cast<const TI*>(a.k.ptr) + b * a.k.sb + head * a.k.sh;
-  const TI* vb = reinterpret_cast<const TI*>(a.v.ptr) + b * a.v.sb + head * a.v.sh;
-  const TI* dob = reinterpret_cast<const TI*>(a.dout.ptr) + b * a.dout.sb + head * a.dout.sh;
+  const char* qbase = reinterpret_cast<const char*>(a.q.ptr) + (b * a.q.sb + head * a.q.sh) * ESZ;
+  const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * ESZ;
+  const char* vbase = reinterpret_cast<const char*>(a.v.ptr) + (b * a.v.sb + head * a.v.sh) * ESZ;
+  const char* dobase = reinterpret_cast<const char*>(a.dout.ptr) + (b * a.dout.sb + head * a.dout.sh) * ESZ;
+  const Rsrc rq = make_rsrc(qbase, slice_bytes(a.lq, a.q.st, ESZ, D));
+  const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, ESZ, D));
+  const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, ESZ, D));
+  const Rsrc rdo = make_rsrc(dobase, slice_bytes(a.lq, a.dout.st, ESZ, D));
+  const uint32_t qst = (uint32_t)(a.q.st * ESZ), kst = (uint32_t)(a.k.st * ESZ);
+  const uint32_t vst = (uint32_t)(a.v.st * ESZ), dst = (uint32_t)(a.dout.st * ESZ);
   const float* lse_b = a.lse + ((int64_t)b * a.heads + head) * a.lq;
   const float* del_b = a.delta + ((int64_t)b * a.heads + head) * a.lq;
   float* dqb = reinterpret_cast<float*>(a.dq.ptr) + b * a.dq.sb + head * a.dq.sh;
@@ -575,17 +695,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
   if constexpr (BF16) {
 #pragma unroll
     for (int c = 0; c < NKF; ++c) {
-      kf[c] = key_ok ? ld_bf16x8(kb + (int64_t)key * a.k.st + 16 * c + 8 * hf) : zero_bf16x8();
-      vf[c] = key_ok ? ld_bf16x8(vb + (int64_t)key * a.v.st + 16 * c + 8 * hf) : zero_bf16x8();
+      kf[c] = __builtin_bit_cast(bf16x8, bload16(rk, (uint32_t)key * kst + (16 * c + 8 * hf) * 2));
+      vf[c] = __builtin_bit_cast(bf16x8, bload16(rv, (uint32_t)key * vst + (16 * c + 8 * hf) * 2));
     }
   } else {
 #pragma unroll
     for (int c4 = 0; c4 < D / 4; ++c4) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-      if (key_ok) {
-        x = *reinterpret_cast<const f32x4*>(kb + (int64_t)key * a.k.st + 4 * c4);
-        y = *reinterpret_cast<const f32x4*>(vb + (int64_t)key * a.v.st + 4 * c4);
-      }
+      const f32x4 x = bload16f(rk, (uint32_t)key * kst + 16 * c4);
+      const f32x4 y = bload16f(rv, (uint32_t)key * vst + 16 * c4);
       kf[2 * c4] = hf ? x[1] : x[0];
       kf[2 * c4 + 1] = hf ? x[3] : x[2];
       vf[2 * c4] = hf ? y[1] : y[0];
@@ -597,19 +714,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
   constexpr int PAIRS = 2 * NDB / 4;  // per wave: 2 for D=128, 1 for D=64
   const int dq_db = (D == 128) ? w : (w & 1);
   const int dq_qb0 = (D == 128) ? 0 : (w >> 1);
-  // K^T fragments for dQ = dS K (bf16: 8 consecutive keys for one d per lane).
+  const int dcol = dq_db * 32 + l32;
+  // K^T fragments for dQ = dS K (bf16: 8 consecutive keys of one d per lane).
   bf16x8 ktf[BF16 ? BWD_BK / 16 : 1];
   if constexpr (BF16) {
-    const int dcol = dq_db * 32 + l32;
 #pragma unroll
-    for (int jj = 0; jj < BWD_BK / 16; ++jj) {
+    for (int jj = 0; jj < BWD_BK / 16; ++jj)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int kk = k_first + 16 * jj + 8 * hf + i;
-        uint16_t bits = (kk <= k_last) ? kb[(int64_t)kk * a.k.st + dcol] : (uint16_t)0;
-        ktf[jj][i] = __builtin_bit_cast(__bf16, bits);
-      }
-    }
+      for (int i = 0; i < 8; ++i)
+        ktf[jj][i] = __builtin_bit_cast(__bf16, bload2(rk, (uint32_t)(k_first + 16 * jj + 8 * hf + i) * kst + dcol * 2));
   }
 
   f32x16 dk[NDB], dv[NDB];
@@ -629,132 +742,41 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
 
   if (rbeg < rend) {
     const int qt0 = rbeg / BQB, qt1 = (rend - 1) / BQB;
+    QStageBf16<D> stage;
+    if constexpr (BF16) {
+      stage.load(a, rq, rdo, qst, dst, lse_b, del_b, qt0 * BQB, tid);
+      stage.store(smem, tid);
+      __syncthreads();
+    }
     for (int qt = qt0; qt <= qt1; ++qt) {
       const int r0 = qt * BQB;
       const int nrows = min(a.lq - r0, BQB);
+      const int cur = BF16 ? ((qt - qt0) & 1) : 0;
+      char* buf = smem + cur * C::BUF;
+      const bool more = qt < qt1;
       if constexpr (BF16) {
-        bwd_stage_bf16<D>(qb, a.q.st, r0, a.lq, sQ, sQt, tid);
-        bwd_stage_bf16<D>(dob, a.dout.st, r0, a.lq, sDO, sDOt, tid);
+        if (more) stage.load(a, rq, rdo, qst, dst, lse_b, del_b, (qt + 1) * BQB, tid);
       } else {
-        bwd_stage_f32<D>(qb, a.q.st, r0, a.lq, sQ, tid);
-        bwd_stage_f32<D>(dob, a.dout.st, r0, a.lq, sDO, tid);
+        bwd_stage_f32<D>(a, rq, rdo, qst, dst, lse_b, del_b, r0, buf, tid);
+        __syncthreads();
       }
-      if (tid < BQB) {
-        const int r = r0 + tid;
-        if (r < a.lq) {
-          const float l = lse_b[r];
-          sLse[tid] = (l == NEG_INF) ? POS_INF : l * LOG2E;
-          sDel[tid] = del_b[r];
-          const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, r));
-          sLo[tid] = rb.lo;
-          sHi[tid] = rb.hi;
-        } else {
-          sLse[tid] = POS_INF;
-          sDel[tid] = 0.f;
-          sLo[tid] = INT_BIG;
-          sHi[tid] = -1;
-        }
-      }
-      __syncthreads();
+      const char* sQ = buf + C::OFF_Q;
+      const char* sQt = buf + C::OFF_QT;
+      const char* sDO = buf + C::OFF_DO;
+      const char* sDOt = buf + C::OFF_DOT;
+      const float* sLse = reinterpret_cast<const float*>(buf + C::OFF_LSE);
+      const float* sDel = reinterpret_cast<const float*>(buf + C::OFF_DEL);
+      const int* sLo = reinterpret_cast<const int*>(buf + C::OFF_LO);
+      const int* sHi = reinterpret_cast<const int*>(buf + C::OFF_HI);
 
       const int lo_f = sLo[0], hi_f = sHi[0], lo_l = sLo[nrows - 1], hi_l = sHi[nrows - 1];
       const bool wave_empty = !wave_has_keys || kwmax < lo_f || kwmin > hi_l;
       const bool wave_full = (kw0 + 32 <= a.lk) && kwmin >= lo_l && kwmax <= hi_f;
 
-      if (!wave_empty) {
-        // S = Q K^T (rows permuted), P = exp2(S*scale*log2e - lse*log2e).
-        f32x16 p[2];
 #pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-          f32x16 acc = f32x16{};
-          if constexpr (BF16) {
-            const char* qr = sQ + (qbk * 32 + row_perm(l32)) * C::QSTR + hf * 16;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(qr + c * 32), kf[c], acc);
-          } else {
-            const float* qr = reinterpret_cast<const float*>(sQ + (qbk * 32 + row_perm(l32)) * C::QSTR) + hf;
-#pragma unroll
-            for (int t = 0; t < D / 2; ++t) acc = mfma_f32(qr[2 * t], kf[t], acc);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int q = qbk * 32 + reg_row(v, hf);
-            float e = ex2(__builtin_fmaf(acc[v], sl2, -sLse[q]));
-            if (!wave_full) {
-              const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
-              e = ok ? e : 0.f;
-            }
-            p[qbk][v] = e;
-          }
-        }
-        // dP = dO V^T (rows permuted), dS = P * (dP - delta).
-        f32x16 ds[2];
-#pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-          f32x16 acc = f32x16{};
-          if constexpr (BF16) {
-            const char* dr = sDO + (qbk * 32 + row_perm(l32)) * C::QSTR + hf * 16;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(ld_bf16x8(dr + c * 32), vf[c], acc);
-          } else {
-            const float* dr = reinterpret_cast<const float*>(sDO + (qbk * 32 + row_perm(l32)) * C::QSTR) + hf;
-#pragma unroll
-            for (int t = 0; t < D / 2; ++t) acc = mfma_f32(dr[2 * t], vf[t], acc);
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int q = qbk * 32 + reg_row(v, hf);
-            ds[qbk][v] = p[qbk][v] * (acc[v] - sDel[q]);
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (K-dim = query rows).
-#pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-          if constexpr (BF16) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              bf16x8 pb, sb;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                pb[i] = (__bf16)p[qbk][8 * u + i];
-                sb[i] = (__bf16)ds[qbk][8 * u + i];
-              }
-              const int qcol = qbk * 32 + 16 * u + 8 * hf;
-#pragma unroll
-              for (int d = 0; d < NDB; ++d) {
-                dv[d] = mfma_bf16(ld_bf16x8(sDOt + tr_off(d * 32 + l32, qcol)), pb, dv[d]);
-                dk[d] = mfma_bf16(ld_bf16x8(sQt + tr_off(d * 32 + l32, qcol)), sb, dk[d]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-              const int q = qbk * 32 + reg_row(t, hf);
-              const float* dor = reinterpret_cast<const float*>(sDO + q * C::QSTR) + l32;
-              const float* qr = reinterpret_cast<const float*>(sQ + q * C::QSTR) + l32;
-#pragma unroll
-              for (int d = 0; d < NDB; ++d) {
-                dv[d] = mfma_f32(dor[d * 32], p[qbk][t], dv[d]);
-                dk[d] = mfma_f32(qr[d * 32], ds[qbk][t], dk[d]);
-              }
-            }
-          }
-        }
-        // dS -> LDS [query][key] for the dQ product.
-#pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int q = qbk * 32 + reg_row(v, hf);
-            if constexpr (BF16)
-              *reinterpret_cast<__bf16*>(sDS + q * C::SSTR + (32 * w + l32) * 2) = (__bf16)ds[qbk][v];
-            else
-              *reinterpret_cast<float*>(sDS + q * C::SSTR + (32 * w + l32) * 4) = ds[qbk][v];
-          }
-      } else {
-        // A wave with nothing visible still provides its (zero) dS columns.
-#pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk)
+      for (int qbk = 0; qbk < 2; ++qbk) {
+        if (wave_empty) {
+          // A wave with nothing visible still provides its (zero) dS columns.
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int q = qbk * 32 + reg_row(v, hf);
@@ -763,6 +785,77 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
             else
               *reinterpret_cast<float*>(sDS + q * C::SSTR + (32 * w + l32) * 4) = 0.f;
           }
+          continue;
+        }
+        // S = Q K^T (rows permuted) and dP = dO V^T.
+        f32x16 s = f32x16{}, dp = f32x16{};
+        if constexpr (BF16) {
+          const char* qr = sQ + (qbk * 32 + row_perm(l32)) * C::QSTR + hf * 16;
+          const char* dr = sDO + (qbk * 32 + row_perm(l32)) * C::QSTR + hf * 16;
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) s = mfma_bf16(ld_bf16x8(qr + c * 32), kf[c], s);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) dp = mfma_bf16(ld_bf16x8(dr + c * 32), vf[c], dp);
+        } else {
+          const float* qr = reinterpret_cast<const float*>(sQ + (qbk * 32 + row_perm(l32)) * C::QSTR) + hf;
+          const float* dr = reinterpret_cast<const float*>(sDO + (qbk * 32 + row_perm(l32)) * C::QSTR) + hf;
+#pragma unroll
+          for (int t = 0; t < D / 2; ++t) s = mfma_f32(qr[2 * t], kf[t], s);
+#pragma unroll
+          for (int t = 0; t < D / 2; ++t) dp = mfma_f32(dr[2 * t], vf[t], dp);
+        }
+        // P = exp2(S*scale*log2e - lse*log2e); dS = P * (dP - delta).
+        f32x16 p, ds;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int q = qbk * 32 + reg_row(v, hf);
+          float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q]));
+          if (!wave_full) {
+            const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
+            e = ok ? e : 0.f;
+          }
+          p[v] = e;
+          ds[v] = e * (dp[v] - sDel[q]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (K-dim = query rows).
+        if constexpr (BF16) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            bf16x8 pb, sb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              pb[i] = (__bf16)p[8 * u + i];
+              sb[i] = (__bf16)ds[8 * u + i];
+            }
+            const int qcol = qbk * 32 + 16 * u + 8 * hf;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) {
+              dv[d] = mfma_bf16(ld_bf16x8(sDOt + tr_off(d * 32 + l32, qcol)), pb, dv[d]);
+              dk[d] = mfma_bf16(ld_bf16x8(sQt + tr_off(d * 32 + l32, qcol)), sb, dk[d]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int q = qbk * 32 + reg_row(t, hf);
+            const float* dor = reinterpret_cast<const float*>(sDO + q * C::QSTR) + l32;
+            const float* qr = reinterpret_cast<const float*>(sQ + q * C::QSTR) + l32;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) {
+              dv[d] = mfma_f32(dor[d * 32], p[t], dv[d]);
+              dk[d] = mfma_f32(qr[d * 32], ds[t], dk[d]);
+            }
+          }
+        }
+        // dS -> LDS [query][key] for the dQ product.
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int q = qbk * 32 + reg_row(v, hf);
+          if constexpr (BF16)
+            *reinterpret_cast<__bf16*>(sDS + q * C::SSTR + (32 * w + l32) * 2) = (__bf16)ds[v];
+          else
+            *reinterpret_cast<float*>(sDS + q * C::SSTR + (32 * w + l32) * 4) = ds[v];
+        }
       }
       __syncthreads();
 
@@ -777,19 +870,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
           for (int jj = 0; jj < BWD_BK / 16; ++jj) acc = mfma_bf16(ld_bf16x8(sr + jj * 32), ktf[jj], acc);
         } else {
           const float* sr = reinterpret_cast<const float*>(sDS + (qbk * 32 + l32) * C::SSTR) + hf;
-          const int dcol = dq_db * 32 + l32;
-          for (int t = 0; t < BWD_BK / 2; ++t) {
-            const int kk = k_first + 2 * t + hf;
-            const float kv = (kk <= k_last) ? kb[(int64_t)kk * a.k.st + dcol] : 0.f;
-            acc = mfma_f32(sr[2 * t], kv, acc);
-          }
+#pragma unroll 8
+          for (int t = 0; t < BWD_BK / 2; ++t)
+            acc = mfma_f32(sr[2 * t], bload4f(rk, (uint32_t)(k_first + 2 * t + hf) * kst + dcol * 4), acc);
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int q = qbk * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
           const int r = r0 + q;
-          if (r < a.lq) atomicAdd(dqb + (int64_t)r * a.dq.st + dq_db * 32 + l32, acc[v] * a.scale);
+          if (r < a.lq) atomicAdd(dqb + (int64_t)r * a.dq.st + dcol, acc[v] * a.scale);
         }
+      }
+      if constexpr (BF16) {
+        if (more) stage.store(smem + (cur ^ 1) * C::BUF, tid);
       }
       __syncthreads();
     }
