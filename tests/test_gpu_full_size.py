@@ -1,0 +1,166 @@
+"""Parity at the full benchmark sizes (32 heads, head_dim 128, bf16 N(0,1)),
+in the launch configuration the benchmark times (ra_ring_fwd / ra_ring_bwd on
+resident rank-major K/V rings).
+
+The float64 oracle cannot redo every output at these sizes, so:
+* forward: sampled query rows (tile, chunk and segment boundaries plus seeded
+  random rows) on sampled heads are recomputed exactly by the oracle;
+* backward: dQ of sampled rows is recomputed exactly (a row's dQ depends only
+  on that row), and dK/dV are checked on every head through identities that
+  hold at any size: the rank's contributions satisfy sum_j dK_j = 0 and
+  sum_j dV_j = sum_i dO_i (each row of P sums to one, each row of dS to zero).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check_grad, check_lse, check_out, dev, f64, log, ring_from_global
+
+pytestmark = pytest.mark.gpu
+
+H, D = 32, 128
+HEADS = [0, 17, 31]
+
+
+def _ra():
+    import exact_long_context_ra_amd as ra
+    return ra
+
+
+def _sample_rows(L, seed, extra=()):
+    base = {0, 1, 31, 32, 63, 64, 127, 128, L // 2 - 1, L // 2, L - 2, L - 1, *extra}
+    rng = np.random.default_rng(seed)
+    base.update(rng.integers(0, L, 16).tolist())
+    return np.array(sorted(r for r in base if 0 <= r < L), dtype=np.int64)
+
+
+def _setup(layout, S, N, seed, cu=None):
+    import torch
+    q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=seed, device=dev(), with_dout=True)
+    kr, idx = ring_from_global(k, layout, N)
+    vr, _ = ring_from_global(v, layout, N)
+    # host float64 copies of the sampled heads only
+    hsel = torch.tensor(HEADS, device=dev())
+    k64 = f64(k.index_select(2, hsel))
+    v64 = f64(v.index_select(2, hsel))
+    return q, do, kr, vr, idx, k64, v64, hsel
+
+
+def _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, cu, what):
+    import torch
+    S = k64.shape[1]
+    gidx = torch.from_numpy(pos[rows]).to(q.device)
+    qr = f64(q.index_select(2, hsel).index_select(1, gidx))
+    ro, rl = oracle.attention(qr, k64, v64, pos[rows], np.arange(S), True, cu)
+    got_o = f64(out.index_select(2, hsel))[:, rows]
+    got_l = f64(lse.index_select(1, hsel))[:, :, rows]
+    check_out(got_o, ro, True, what=f"{what} out")
+    check_lse(got_l, rl, True, what=f"{what} lse")
+    return ro, rl
+
+
+def _check_invariants(dk_ring, dv_ring, dol, out_has_keys, what):
+    """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i over the rank's rows (per head, per d)."""
+    dk = dk_ring.double().sum(dim=(0, 2))   # [b, h, d]
+    dv = dv_ring.double().sum(dim=(0, 2))
+    dks = dk_ring.double().abs().sum(dim=(0, 2))
+    dvs = dv_ring.double().abs().sum(dim=(0, 2))
+    want_dv = (dol.double() * out_has_keys[None, :, None, None]).sum(dim=1)
+    err_k = float((dk.abs() / (dks + 1e-30)).max())
+    err_v = float(((dv - want_dv).abs() / (dvs + 1e-30)).max())
+    log(f"{what}: sum dK rel {err_k:.2e}, sum dV rel {err_v:.2e}")
+    assert err_k <= 1e-3, f"{what}: sum_j dK_j = {err_k:.3e} of sum |dK|"
+    assert err_v <= 1e-3, f"{what}: sum_j dV_j - sum_i dO_i = {err_v:.3e} of sum |dV|"
+
+
+def _check_dq_rows(q, do, dq, out_rows_ref, lse_rows_ref, pos, rows, k64, v64, hsel, cu, what):
+    import torch
+    S = k64.shape[1]
+    gidx = torch.from_numpy(pos[rows]).to(q.device)
+    qr = f64(q.index_select(2, hsel).index_select(1, gidx))
+    dor = f64(do.index_select(2, hsel).index_select(1, gidx))
+    gq, _, _ = oracle.attention_backward(qr, k64, v64, out_rows_ref, lse_rows_ref, dor, pos[rows], np.arange(S),
+                                         True, cu)
+    check_grad(f64(dq.index_select(2, hsel))[:, rows], gq, True, what=f"{what} dq")
+
+
+@pytest.mark.parametrize("layout,S,rank", [("zigzag", 131072, 0), ("zigzag", 131072, 5),
+                                           ("stripe", 262144, 0)])
+def test_full_size_fwd_bwd(layout, S, rank):
+    import torch
+    ra = _ra()
+    N = 8
+    log(f"full-size {layout} S={S} rank={rank}")
+    q, do, kr, vr, idx, k64, v64, hsel = _setup(layout, S, N, seed=0)
+    ql = q.index_select(1, idx[rank]).contiguous()
+    dol = do.index_select(1, idx[rank]).contiguous()
+    out, lse, _ = ra.ring_fwd(layout, N, rank, ql, kr, vr, causal=True)
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
+    dq, _, _ = ra.ring_bwd(layout, N, rank, ql, kr, vr, out, lse, dol, causal=True, dk_ring=dk_ring,
+                           dv_ring=dv_ring)
+    torch.cuda.synchronize()
+    pos = oracle.layout_positions(layout, S, N, rank)
+    L = S // N
+    rows = _sample_rows(L, seed=rank + 1, extra=(L // 2 + 1,))
+    # q/do are the global tensors: the checks take rows by global position
+    ro, rl = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, None, f"{layout} r{rank}")
+    _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, None, f"{layout} r{rank}")
+    has = torch.ones(L, device=dev(), dtype=torch.float64)  # causal self-attention: every row sees itself
+    _check_invariants(dk_ring, dv_ring, dol, has, f"{layout} r{rank}")
+
+
+def test_full_size_contiguous_all_ranks():
+    """Contiguous causal ring over 32768 tokens: every rank's forward share."""
+    import torch
+    ra = _ra()
+    layout, S, N = "contiguous", 32768, 8
+    log("full-size contiguous S=32768 all ranks")
+    q, do, kr, vr, idx, k64, v64, hsel = _setup(layout, S, N, seed=0)
+    L = S // N
+    for r in range(N):
+        ql = q.index_select(1, idx[r]).contiguous()
+        out, lse, lowp = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True, want_lowp=True)
+        torch.cuda.synchronize()
+        pos = oracle.layout_positions(layout, S, N, r)
+        rows = _sample_rows(L, seed=10 + r)
+        ro, _ = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, None, f"contiguous r{r}")
+        check_out(f64(lowp.index_select(2, hsel))[:, rows], ro, True, what=f"contiguous r{r} out_lowp")
+
+
+def test_full_size_varlen_all_slices():
+    """Packed varlen (131072 tokens, log-uniform lengths in [1024, 32768], seed 0),
+    8 contiguous query slices each attending to all K/V of their sequences."""
+    import torch
+    ra = _ra()
+    layout, S, N = "contiguous", 131072, 8
+    lengths = synth.loguniform_lengths(S, 1024, 32768, seed=0)
+    cu = synth.cu_seqlens(lengths)
+    log(f"full-size varlen {len(lengths)} sequences")
+    q, do, kr, vr, idx, k64, v64, hsel = _setup(layout, S, N, seed=0, cu=cu)
+    L = S // N
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
+    for r in range(N):
+        ql = q.index_select(1, idx[r]).contiguous()
+        dol = do.index_select(1, idx[r]).contiguous()
+        out, lse, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True, cu_seqlens=cu)
+        dk_r = torch.zeros_like(dk_ring)
+        dv_r = torch.zeros_like(dv_ring)
+        dq, _, _ = ra.ring_bwd(layout, N, r, ql, kr, vr, out, lse, dol, causal=True, cu_seqlens=cu,
+                               dk_ring=dk_r, dv_ring=dv_r)
+        torch.cuda.synchronize()
+        pos = oracle.layout_positions(layout, S, N, r)
+        starts = [int(c) - r * L for c in cu[:-1] if r * L <= c < (r + 1) * L]
+        rows = _sample_rows(L, seed=20 + r, extra=tuple(starts) + tuple(s + 1 for s in starts))
+        ro, rl = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, cu, f"varlen r{r}")
+        if r in (0, 5):
+            _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, cu, f"varlen r{r}")
+        has = torch.ones(L, device=dev(), dtype=torch.float64)
+        _check_invariants(dk_r, dv_r, dol, has, f"varlen r{r}")
+        dk_ring += dk_r
+        dv_ring += dv_r
+    # all slices together: the complete gradients, still satisfying the identities
+    _check_invariants(dk_ring, dv_ring, do.index_select(1, torch.cat(idx)), torch.ones(S, device=dev(),
+                      dtype=torch.float64), "varlen all slices")
