@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="zigzag", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run one plain device copy of MIB MiB (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (the virtual ring runs every ring step on it); "
@@ -114,6 +116,15 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     layout, S, N, ranks, varlen = WORKLOADS[args.workload]
     H, D = HEADS, HEAD_DIM
     L = S // N
@@ -186,13 +197,18 @@ def main():
         agg = per_kernel.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0})
         agg["launches"] += 1
         agg["ms"] += ms
-    # FLOPs per kernel over the timed region
-    fwd_k = 4.0 * D * H * total_pairs * args.steps
-    per_kernel.setdefault("block_fwd", {"launches": 0, "ms": 0.0, "flops": 0.0})["flops"] = fwd_k
-    per_kernel.setdefault("block_bwd", {"launches": 0, "ms": 0.0, "flops": 0.0})["flops"] = 2.5 * fwd_k
+    # Matrix-product FLOPs each kernel executes over the timed region, per
+    # visible pair and head: forward QK^T + PV = 4*D; the dK/dV kernel
+    # recomputes S and dP and forms dV, dK = 8*D; the dQ kernel recomputes S
+    # and dP and forms dQ = 6*D.  (The metric above counts the backward as
+    # 10*D per pair, the five products of the textbook gradient.)
+    per_pair = {"block_fwd": 4.0, "block_bwd_dkdv": 8.0, "block_bwd_dq": 6.0}
+    for name, f in per_pair.items():
+        per_kernel.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0})["flops"] = (
+            f * D * H * total_pairs * args.steps)
     dom = max(per_kernel, key=lambda n: per_kernel[n]["ms"])
     dk = per_kernel[dom]
-    if dom in ("block_fwd", "block_bwd") and dk["ms"] > 0:
+    if dom in per_pair and dk["ms"] > 0:
         achieved = dk["flops"] / (dk["ms"] / 1e3) / 1e12
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": dom,
@@ -229,7 +245,8 @@ def main():
         "pct_peak_fwd": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "ms_fwd": round(ms_fwd, 3),
         "visible_pairs_per_head": total_pairs,
-        "kernels": {n: {"launches": a["launches"], "avg_ms": round(a["ms"] / max(1, a["launches"]), 4)}
+        "kernels": {n: {"launches": a["launches"], "avg_ms": round(a["ms"] / max(1, a["launches"]), 4),
+                        **({"tflops": round(a["flops"] / (a["ms"] / 1e3) / 1e12, 1)} if a["flops"] and a["ms"] else {})}
                     for n, a in per_kernel.items() if a["launches"]},
         "roofline": roofline,
         "cpu_baseline": None,

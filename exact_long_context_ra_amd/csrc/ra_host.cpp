@@ -16,7 +16,7 @@
 
 #include <vector>
 
-#include "../../include/ra.h"
+#include "ra.h"
 #include "ra_internal.h"
 
 using namespace ra;
@@ -301,7 +301,8 @@ int ra_abi_version(void) { return RA_ABI_VERSION; }
 const char* ra_kernel_name(int32_t id) {
   switch (id) {
     case K_FWD: return "block_fwd";
-    case K_BWD: return "block_bwd";
+    case K_BWD: return "block_bwd_dkdv";
+    case K_BWD_DQ: return "block_bwd_dq";
     case K_MERGE: return "lse_merge";
     case K_PREP: return "bwd_preprocess";
     case K_FILL: return "fill";
@@ -457,6 +458,17 @@ ra_status ra_bwd_preprocess(const ra_problem* prob, int64_t lq, ra_tensor out, r
   return RA_OK;
 }
 
+// One backward block step: bf16 runs the dK/dV and dQ kernels, fp32 the fused kernel.
+static ra_status launch_bwd_step(const BwdArgs& a, int head_dim, bool bf16, int step, hipStream_t s) {
+  if (bf16) {
+    RA_HIP(timed(K_BWD, step, s, [&] { return launch_bwd_dkdv(a, head_dim, s); }));
+    RA_HIP(timed(K_BWD_DQ, step, s, [&] { return launch_bwd_dq(a, head_dim, s); }));
+  } else {
+    RA_HIP(timed(K_BWD, step, s, [&] { return launch_bwd_fused_f32(a, head_dim, s); }));
+  }
+  return RA_OK;
+}
+
 static ra_status bwd_args(const ra_problem* prob, ra_tensor q, int64_t lq, const ra_posmap& qmap, Tensor4 k,
                           Tensor4 v, int64_t lk, const ra_posmap& kmap, ra_tensor dout, const float* lse,
                           const float* delta, Tensor4W dq, Tensor4W dk, Tensor4W dv, BwdArgs* out) {
@@ -480,6 +492,7 @@ static ra_status bwd_args(const ra_problem* prob, ra_tensor q, int64_t lq, const
   a.scale = scale_of(prob);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.n_ktiles = ceil_div(lk, BWD_BK);
+  a.n_qtiles = ceil_div(lq, FWD_BQ);
   *out = a;
   return RA_OK;
 }
@@ -507,8 +520,7 @@ ra_status ra_block_attn_bwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_
   bwd_args(prob, q, lq, qmap, rd(k), rd(v), lk, kmap, dout, lse, delta, wr(dq_acc), wr(dk_acc), wr(dv_acc), &a);
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = prob->dtype == RA_DTYPE_BF16;
-  RA_HIP(timed(K_BWD, -1, s, [&] { return launch_bwd(a, prob->head_dim, bf16, s); }));
-  return RA_OK;
+  return launch_bwd_step(a, prob->head_dim, bf16, -1, s);
 }
 
 // ---- virtual ring -------------------------------------------------------------------------
@@ -644,7 +656,8 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     bwd_args(prob, q_local, L, qmap, offset_rd(k_ring, src * stride_rank, esz),
              offset_rd(v_ring, src * stride_rank, esz), L, kmap, dout, lse, delta, dqw,
              offset_wr(dk_ring, src * stride_rank_grad, 4), offset_wr(dv_ring, src * stride_rank_grad, 4), &a);
-    RA_HIP(timed(K_BWD, step, s, [&] { return launch_bwd(a, prob->head_dim, bf16, s); }));
+    ra_status st2 = launch_bwd_step(a, prob->head_dim, bf16, step, s);
+    if (st2 != RA_OK) return st2;
   }
   return RA_OK;
 }

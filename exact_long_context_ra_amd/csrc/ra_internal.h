@@ -58,7 +58,8 @@ struct BwdArgs {
   MaskSpec mask;
   float scale;         // softmax_scale
   float scale_log2;    // softmax_scale * log2(e)
-  int32_t n_ktiles;
+  int32_t n_ktiles;    // key tiles (dK/dV and fused kernels)
+  int32_t n_qtiles;    // query tiles (dQ kernel)
 };
 
 struct MergeArgs {
@@ -85,13 +86,14 @@ struct FillArgs {
 // Kernel ids reported by the timing facility.
 enum KernelId : int32_t {
   K_FWD = 0,
-  K_BWD = 1,
+  K_BWD = 1,  // bf16: dK/dV kernel; fp32: fused backward
   K_MERGE = 2,
   K_PREP = 3,
   K_FILL = 4,
   K_CAST = 5,
   K_ZERO = 6,
-  K_COUNT = 7
+  K_BWD_DQ = 7,  // bf16 dQ kernel
+  K_COUNT = 8
 };
 
 // Tile sizes shared by planner and kernels.
@@ -100,7 +102,9 @@ constexpr int BWD_BK = 128;  // key rows per backward workgroup
 
 // Launchers (ra_kernels.hip).  Return the launch status; the caller checks it.
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_bwd_fused_f32(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fill(const FillArgs& a, hipStream_t s);

@@ -908,6 +908,605 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
 }
 
 // ============================================================================================
+// bf16 tiles in LDS.  Every tile is stored in its natural [row][D] layout with
+// the 16-byte chunks of each row XOR-swizzled, filled by direct buffer->LDS
+// loads (no registers, no VALU) and read two ways:
+//  * as MFMA rows: lane (row, half) reads 16 bytes = 8 consecutive elements of
+//    one row (A operand of S^T = K Q^T, S = Q K^T, dP = dO V^T, ...);
+//  * transposed, with the LDS transpose read: in each 16-lane group lane i
+//    receives element (i mod 4) of the 8-byte chunk addressed by group lane
+//    4r + i/4, for r = 0..3.  Pointing group lane j at row key0 + j/4, columns
+//    4(j mod 4).. of the group's 16 columns gives every lane 4 consecutive rows
+//    of ONE column; two such reads form an MFMA operand whose K-dim runs over
+//    rows (V^T for O^T += V^T P^T, K^T for dQ, Q^T / dO^T for dK / dV).
+// The swizzle keeps both read patterns free of LDS bank conflicts: the 16 rows
+// a 16-lane set reads as MFMA rows hit 16 distinct chunk positions, and the
+// 4 rows x 2 chunks of a transposed read hit 8 distinct positions.
+// ============================================================================================
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  else return (r >> 1) & 7;
+}
+// Byte offset of 16-byte chunk `chunk` of row `row` in a swizzled [rows][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int nat_off(int row, int chunk) {
+  return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
+}
+__device__ __forceinline__ u32x2 tr16(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p)));
+}
+// MFMA operand from a transposed read: rows key0 .. key0+7 (key0 already holds
+// the lane half's offset) of column 32*db + (lane mod 32).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int key0, int db, int lane) {
+  const int j = lane & 15, g1 = (lane >> 4) & 1;
+  const int colb = 2 * (32 * db + 16 * g1 + 4 * (j & 3));
+  const int chunk = colb >> 4, within = colb & 15;
+  const u32x2 lo = tr16(tile + nat_off<D>(key0 + (j >> 2), chunk) + within);
+  const u32x2 hi = tr16(tile + nat_off<D>(key0 + 4 + (j >> 2), chunk) + within);
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+// 8 consecutive elements (16-byte chunk 2c + hf) of row `row`: an MFMA row operand.
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const char* tile, int row, int c, int hf) {
+  return ld_bf16x8(tile + nat_off<D>(row, 2 * c + hf));
+}
+// Direct buffer->LDS copy of rows [r0, r0 + ROWS) of a [rows][D] bf16 slice into
+// a swizzled tile; wave w moves rows [w*ROWS/4, (w+1)*ROWS/4).  Rows past the
+// slice read as zeros (buffer range check).  `w` must be wave-uniform.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_tile(Rsrc rs, uint32_t st, int r0, char* tile, int w, int lane) {
+  constexpr int RPI = 1024 / (2 * D);  // rows per instruction (64 lanes x 16 bytes)
+  constexpr int CPR = (2 * D) / 16;    // chunks per row
+  constexpr int RPW = ROWS / 4;        // rows per wave
+  static_assert(RPW % RPI == 0, "tile rows must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < RPW / RPI; ++i) {
+    const int rbase = w * RPW + i * RPI;
+    const int row = rbase + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + rbase * 2 * D), 16,
+                                             (uint32_t)(r0 + row) * st + c * 16, 0, 0, 0);
+  }
+}
+// Wait for this wave's outstanding global/buffer loads (including buffer->LDS).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ============================================================================================
+// bf16 forward: tiles of 64 keys, K and V DMA'd one tile ahead into the other
+// of two LDS buffers; one barrier per tile.
+// ============================================================================================
+
+template <int D>
+struct FwdB {
+  static constexpr int TILE = FBK * D * 2;  // bytes of one K (or V) tile
+  static constexpr int BUF = 2 * TILE;      // K then V
+  static constexpr int LDS = 2 * BUF;
+};
+
+template <int D>
+__device__ __forceinline__ void fwd_tile_bf16(const FwdArgs& a, int j0, const char* sK, const char* sV,
+                                              const bf16x8* qf, const Bounds& rb, const Bounds& wv_f,
+                                              const Bounds& wv_l, bool wave_has_rows, float& m_run, float& l_run,
+                                              f32x16* o, int lane, int l32, int hf) {
+  constexpr int NDB = D / 32;
+  const int jl = min(a.lk, j0 + FBK) - 1;
+  const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
+  if (!wave_has_rows || kmax < wv_f.lo || kmin > wv_l.hi) return;  // nothing visible to this wave
+  const bool wave_full = (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
+  const float sl2 = a.scale_log2;
+
+  f32x16 st[2];
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    f32x16 acc = f32x16{};
+    const int row = c2 * 32 + row_perm(l32);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(row_operand<D>(sK, row, c, hf), qf[c], acc);
+    st[c2] = acc;
+  }
+  if (!wave_full) {
+    const bool in0 = j0 < a.kmap.s0.len;
+    const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
+    const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = j0 + c2 * 32 + reg_row(v, hf);
+        const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
+        const bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+        st[c2][v] = ok ? st[c2][v] : NEG_INF;
+      }
+  }
+  float mx = NEG_INF;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  const bool grow = mx > m_run + RESCALE_TH;
+  if (__any(grow)) {
+    const float m_new = grow ? mx : m_run;
+    const float alpha = (m_new == m_run) ? 1.f : ex2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+  float rs = 0.f;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = ex2(__builtin_fmaf(st[c2][v], sl2, -m_use));
+      st[c2][v] = p;
+      rs += p;
+    }
+  l_run += rs;
+  // O^T += V^T P^T (V^T through the transposed read of the natural V tile)
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
+      const int key0 = c2 * 32 + 16 * u + 8 * hf;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) o[d] = mfma_bf16(tr_operand<D>(sV, key0, d, lane), pb, o[d]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
+  using C = FwdB<D>;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;  // latest (heaviest causal) tiles first
+  const int bh = logical / a.n_qtiles;
+  const int head = bh % a.heads, b = bh / a.heads;
+
+  const int r_first = qt * FWD_BQ;
+  const int r_last = min(a.lq, r_first + FWD_BQ) - 1;
+  const int w_first = r_first + 32 * w;
+  const int w_last = min(r_last, w_first + 31);
+  const bool wave_has_rows = w_first <= r_last;
+  const int row = w_first + l32;
+  const bool row_ok = row <= r_last;
+
+  const char* qbase = reinterpret_cast<const char*>(a.q.ptr) + (b * a.q.sb + head * a.q.sh) * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v.ptr) + (b * a.v.sb + head * a.v.sh) * 2;
+  const Rsrc rq = make_rsrc(qbase, slice_bytes(a.lq, a.q.st, 2, D));
+  const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
+  const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, 2, D));
+  const uint32_t qst = (uint32_t)(a.q.st * 2), kst = (uint32_t)(a.k.st * 2), vst = (uint32_t)(a.v.st * 2);
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    qf[c] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)row * qst + (16 * c + 8 * hf) * 2));
+
+  const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, min(row, r_last)));
+  const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
+  const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
+  const Bounds wv_f = row_bounds(a.mask, map_pos(a.qmap, min(w_first, r_last)));
+  const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
+  const int kbeg = first_ge(a.kmap, wg_f.lo);
+  const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+
+  float m_run = NEG_INF, l_run = 0.f;
+  f32x16 o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) o[d] = f32x16{};
+
+  if (kbeg < kend) {
+    const int jt0 = kbeg / FBK, jt1 = (kend - 1) / FBK;
+    dma_tile<D, FBK>(rk, kst, jt0 * FBK, smem, w, lane);
+    dma_tile<D, FBK>(rv, vst, jt0 * FBK, smem + C::TILE, w, lane);
+    wait_vmem();
+    __syncthreads();
+    for (int jt = jt0; jt <= jt1; ++jt) {
+      const int cur = (jt - jt0) & 1;
+      const char* sK = smem + cur * C::BUF;
+      if (jt < jt1) {
+        char* nK = smem + (cur ^ 1) * C::BUF;
+        dma_tile<D, FBK>(rk, kst, (jt + 1) * FBK, nK, w, lane);
+        dma_tile<D, FBK>(rv, vst, (jt + 1) * FBK, nK + C::TILE, w, lane);
+      }
+      fwd_tile_bf16<D>(a, jt * FBK, sK, sK + C::TILE, qf, rb, wv_f, wv_l, wave_has_rows, m_run, l_run, o, lane,
+                       l32, hf);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  float lse_b, inv;
+  if (l_tot > 0.f) {
+    lse_b = (m_run + __log2f(l_tot)) * LN2;
+    inv = 1.f / l_tot;
+  } else {
+    lse_b = NEG_INF;
+    inv = 0.f;
+  }
+  float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lq + row;
+  float* orow = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)row * a.out.st + head * a.out.sh;
+  float wa = 0.f, wb = inv, lse_new = lse_b;
+  if (a.mode == FWD_MERGE) {
+    const float lse_old = *lse_p;
+    const float mm = fmaxf(lse_old, lse_b);
+    if (mm == NEG_INF) {
+      wa = 0.f;
+      wb = 0.f;
+      lse_new = NEG_INF;
+    } else {
+      const float ea = expf(lse_old - mm), eb = expf(lse_b - mm);
+      const float s = ea + eb;
+      lse_new = mm + logf(s);
+      wa = ea / s;
+      wb = eb / s * inv;
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = d * 32 + 8 * g + 4 * hf;
+      f32x4 val = {o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb};
+      if (a.mode == FWD_MERGE) val += wa * *reinterpret_cast<const f32x4*>(orow + d0);
+      *reinterpret_cast<f32x4*>(orow + d0) = val;
+      if (a.out_lowp.ptr) {
+        uint16_t* lp = reinterpret_cast<uint16_t*>(a.out_lowp.ptr) + b * a.out_lowp.sb +
+                       (int64_t)row * a.out_lowp.st + head * a.out_lowp.sh + d0;
+        const __bf16 t0 = (__bf16)val[0], t1 = (__bf16)val[1], t2 = (__bf16)val[2], t3 = (__bf16)val[3];
+        const uint32_t p0 =
+            (uint32_t)__builtin_bit_cast(uint16_t, t0) | ((uint32_t)__builtin_bit_cast(uint16_t, t1) << 16);
+        const uint32_t p1 =
+            (uint32_t)__builtin_bit_cast(uint16_t, t2) | ((uint32_t)__builtin_bit_cast(uint16_t, t3) << 16);
+        *reinterpret_cast<u32x2*>(lp) = u32x2{p0, p1};
+      }
+    }
+  }
+  if (hf == 0) *lse_p = lse_new;
+}
+
+// ============================================================================================
+// bf16 backward, split into two kernels without any atomics (on this GPU a
+// device-wide float atomic is performed past the L2, which caps a fused
+// backward's dQ accumulation far below the MFMA rate):
+//  * dK/dV kernel: a workgroup owns 128 keys (32 per wave) and walks the query
+//    tiles that can see them: S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
+//    dK^T += Q^T dS.  Q/dO tiles are DMA'd one tile ahead.
+//  * dQ kernel: a workgroup owns 128 query rows (32 per wave) and walks the
+//    key tiles they can see: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T,
+//    dQ^T += K^T dS^T.  K/V tiles are DMA'd one tile ahead.
+// Both recompute P from the final lse; S and dP are computed twice (7 matrix
+// products per pair instead of 5), bought back by the absence of atomics and
+// by each kernel's smaller register and LDS footprint.
+// ============================================================================================
+
+constexpr int DQ_BK = 64;  // keys per dQ-kernel tile
+
+template <int D>
+struct DkdvB {
+  static constexpr int TILE = BQB * D * 2;
+  static constexpr int OFF_DO = TILE;
+  static constexpr int OFF_ROWS = 2 * TILE;  // lse*log2e, delta, lo, hi (64 each)
+  static constexpr int BUF = OFF_ROWS + 4 * BQB * 4;
+  static constexpr int LDS = 2 * BUF;
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = DkdvB<D>;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int kt = logical % a.n_ktiles;  // earliest (heaviest causal) key tiles first
+  const int bh = logical / a.n_ktiles;
+  const int head = bh % a.heads, b = bh / a.heads;
+
+  const char* qbase = reinterpret_cast<const char*>(a.q.ptr) + (b * a.q.sb + head * a.q.sh) * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v.ptr) + (b * a.v.sb + head * a.v.sh) * 2;
+  const char* dobase = reinterpret_cast<const char*>(a.dout.ptr) + (b * a.dout.sb + head * a.dout.sh) * 2;
+  const Rsrc rq = make_rsrc(qbase, slice_bytes(a.lq, a.q.st, 2, D));
+  const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
+  const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, 2, D));
+  const Rsrc rdo = make_rsrc(dobase, slice_bytes(a.lq, a.dout.st, 2, D));
+  const uint32_t qst = (uint32_t)(a.q.st * 2), kst = (uint32_t)(a.k.st * 2);
+  const uint32_t vst = (uint32_t)(a.v.st * 2), dst = (uint32_t)(a.dout.st * 2);
+  const float* lse_b = a.lse + ((int64_t)b * a.heads + head) * a.lq;
+  const float* del_b = a.delta + ((int64_t)b * a.heads + head) * a.lq;
+
+  const int k_first = kt * BWD_BK;
+  const int k_last = min(a.lk, k_first + BWD_BK) - 1;
+  const int kw0 = k_first + 32 * w;
+  const int kw_last = min(k_last, kw0 + 31);
+  const bool wave_has_keys = kw0 <= k_last;
+  const int key = kw0 + l32;
+  const bool key_ok = key <= k_last;
+  const int kpos = map_pos(a.kmap, min(key, k_last));
+
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    kf[c] = __builtin_bit_cast(bf16x8, bload16(rk, (uint32_t)key * kst + (16 * c + 8 * hf) * 2));
+    vf[c] = __builtin_bit_cast(bf16x8, bload16(rv, (uint32_t)key * vst + (16 * c + 8 * hf) * 2));
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    dk[d] = f32x16{};
+    dv[d] = f32x16{};
+  }
+
+  const Bounds cf = col_bounds(a.mask, map_pos(a.kmap, k_first));
+  const Bounds cl = col_bounds(a.mask, map_pos(a.kmap, k_last));
+  const int rbeg = first_ge(a.qmap, cf.lo);
+  const int rend = min(a.lq, last_le(a.qmap, cl.hi) + 1);
+  const int kwmin = map_pos(a.kmap, min(kw0, k_last)), kwmax = map_pos(a.kmap, kw_last);
+  const float sl2 = a.scale_log2;
+
+  if (rbeg < rend) {
+    const int qt0 = rbeg / BQB, qt1 = (rend - 1) / BQB;
+    // Per-row data of a query tile travels through registers (threads 0..63).
+    RowStage rows;
+    rows.load(a, lse_b, del_b, qt0 * BQB, tid);
+    dma_tile<D, BQB>(rq, qst, qt0 * BQB, smem, w, lane);
+    dma_tile<D, BQB>(rdo, dst, qt0 * BQB, smem + C::OFF_DO, w, lane);
+    if (tid < BQB) {
+      float* rr = reinterpret_cast<float*>(smem + C::OFF_ROWS);
+      rr[tid] = rows.l;
+      rr[BQB + tid] = rows.dl;
+      reinterpret_cast<int*>(rr)[2 * BQB + tid] = rows.lo;
+      reinterpret_cast<int*>(rr)[3 * BQB + tid] = rows.hi;
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int qt = qt0; qt <= qt1; ++qt) {
+      const int cur = (qt - qt0) & 1;
+      const char* buf = smem + cur * C::BUF;
+      const bool more = qt < qt1;
+      if (more) {
+        char* nb = smem + (cur ^ 1) * C::BUF;
+        rows.load(a, lse_b, del_b, (qt + 1) * BQB, tid);
+        dma_tile<D, BQB>(rq, qst, (qt + 1) * BQB, nb, w, lane);
+        dma_tile<D, BQB>(rdo, dst, (qt + 1) * BQB, nb + C::OFF_DO, w, lane);
+      }
+      const char* sQ = buf;
+      const char* sDO = buf + C::OFF_DO;
+      const float* sLse = reinterpret_cast<const float*>(buf + C::OFF_ROWS);
+      const float* sDel = sLse + BQB;
+      const int* sLo = reinterpret_cast<const int*>(sLse + 2 * BQB);
+      const int* sHi = sLo + BQB;
+      const int nrows = min(a.lq - qt * BQB, BQB);
+      const int lo_f = sLo[0], hi_f = sHi[0], lo_l = sLo[nrows - 1], hi_l = sHi[nrows - 1];
+      const bool wave_empty = !wave_has_keys || kwmax < lo_f || kwmin > hi_l;
+      const bool wave_full = (kw0 + 32 <= a.lk) && kwmin >= lo_l && kwmax <= hi_f;
+      if (!wave_empty) {
+#pragma unroll
+        for (int qbk = 0; qbk < 2; ++qbk) {
+          f32x16 s = f32x16{}, dp = f32x16{};
+          const int qrow = qbk * 32 + row_perm(l32);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), kf[c], s);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), vf[c], dp);
+          f32x16 p, ds;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = qbk * 32 + reg_row(v, hf);
+            float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q]));
+            if (!wave_full) {
+              const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
+              e = ok ? e : 0.f;
+            }
+            p[v] = e;
+            ds[v] = e * (dp[v] - sDel[q]);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            bf16x8 pb, sb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              pb[i] = (__bf16)p[8 * u + i];
+              sb[i] = (__bf16)ds[8 * u + i];
+            }
+            const int q0 = qbk * 32 + 16 * u + 8 * hf;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) {
+              dv[d] = mfma_bf16(tr_operand<D>(sDO, q0, d, lane), pb, dv[d]);
+              dk[d] = mfma_bf16(tr_operand<D>(sQ, q0, d, lane), sb, dk[d]);
+            }
+          }
+        }
+      }
+      if (more && tid < BQB) {
+        float* rr = reinterpret_cast<float*>(smem + (cur ^ 1) * C::BUF + C::OFF_ROWS);
+        rr[tid] = rows.l;
+        rr[BQB + tid] = rows.dl;
+        reinterpret_cast<int*>(rr)[2 * BQB + tid] = rows.lo;
+        reinterpret_cast<int*>(rr)[3 * BQB + tid] = rows.hi;
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  if (!key_ok) return;
+  float* dkr = reinterpret_cast<float*>(a.dk.ptr) + b * a.dk.sb + (int64_t)key * a.dk.st + head * a.dk.sh;
+  float* dvr = reinterpret_cast<float*>(a.dv.ptr) + b * a.dv.sb + (int64_t)key * a.dv.st + head * a.dv.sh;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = d * 32 + 8 * g + 4 * hf;
+      f32x4 x = *reinterpret_cast<const f32x4*>(dkr + d0);
+      f32x4 y = *reinterpret_cast<const f32x4*>(dvr + d0);
+      x += a.scale * f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]};
+      y += f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(dkr + d0) = x;
+      *reinterpret_cast<f32x4*>(dvr + d0) = y;
+    }
+}
+
+template <int D>
+struct DqB {
+  static constexpr int TILE = DQ_BK * D * 2;
+  static constexpr int BUF = 2 * TILE;  // K then V
+  static constexpr int LDS = 2 * BUF;
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
+  using C = DqB<D>;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;
+  const int bh = logical / a.n_qtiles;
+  const int head = bh % a.heads, b = bh / a.heads;
+
+  const int r_first = qt * FWD_BQ;
+  const int r_last = min(a.lq, r_first + FWD_BQ) - 1;
+  const int w_first = r_first + 32 * w;
+  const int w_last = min(r_last, w_first + 31);
+  const bool wave_has_rows = w_first <= r_last;
+  const int row = w_first + l32;
+  const bool row_ok = row <= r_last;
+
+  const char* qbase = reinterpret_cast<const char*>(a.q.ptr) + (b * a.q.sb + head * a.q.sh) * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v.ptr) + (b * a.v.sb + head * a.v.sh) * 2;
+  const char* dobase = reinterpret_cast<const char*>(a.dout.ptr) + (b * a.dout.sb + head * a.dout.sh) * 2;
+  const Rsrc rq = make_rsrc(qbase, slice_bytes(a.lq, a.q.st, 2, D));
+  const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
+  const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, 2, D));
+  const Rsrc rdo = make_rsrc(dobase, slice_bytes(a.lq, a.dout.st, 2, D));
+  const uint32_t qst = (uint32_t)(a.q.st * 2), kst = (uint32_t)(a.k.st * 2);
+  const uint32_t vst = (uint32_t)(a.v.st * 2), dst = (uint32_t)(a.dout.st * 2);
+
+  // B operands: Q^T and dO^T columns of this lane's query row.
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    qf[c] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)row * qst + (16 * c + 8 * hf) * 2));
+    gf[c] = __builtin_bit_cast(bf16x8, bload16(rdo, (uint32_t)row * dst + (16 * c + 8 * hf) * 2));
+  }
+  float lse2 = POS_INF, dl = 0.f;
+  if (row_ok) {
+    const float x = a.lse[((int64_t)b * a.heads + head) * a.lq + row];
+    lse2 = (x == NEG_INF) ? POS_INF : x * LOG2E;
+    dl = a.delta[((int64_t)b * a.heads + head) * a.lq + row];
+  }
+
+  const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, min(row, r_last)));
+  const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
+  const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
+  const Bounds wv_f = row_bounds(a.mask, map_pos(a.qmap, min(w_first, r_last)));
+  const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
+  const int kbeg = first_ge(a.kmap, wg_f.lo);
+  const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+  const float sl2 = a.scale_log2;
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) dq[d] = f32x16{};
+
+  if (kbeg < kend) {
+    const int jt0 = kbeg / DQ_BK, jt1 = (kend - 1) / DQ_BK;
+    dma_tile<D, DQ_BK>(rk, kst, jt0 * DQ_BK, smem, w, lane);
+    dma_tile<D, DQ_BK>(rv, vst, jt0 * DQ_BK, smem + C::TILE, w, lane);
+    wait_vmem();
+    __syncthreads();
+    for (int jt = jt0; jt <= jt1; ++jt) {
+      const int cur = (jt - jt0) & 1;
+      const char* sK = smem + cur * C::BUF;
+      const char* sV = sK + C::TILE;
+      if (jt < jt1) {
+        char* nK = smem + (cur ^ 1) * C::BUF;
+        dma_tile<D, DQ_BK>(rk, kst, (jt + 1) * DQ_BK, nK, w, lane);
+        dma_tile<D, DQ_BK>(rv, vst, (jt + 1) * DQ_BK, nK + C::TILE, w, lane);
+      }
+      const int j0 = jt * DQ_BK;
+      const int jl = min(a.lk, j0 + DQ_BK) - 1;
+      const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
+      if (wave_has_rows && kmax >= wv_f.lo && kmin <= wv_l.hi) {
+        const bool wave_full = (j0 + DQ_BK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
+        const bool in0 = j0 < a.kmap.s0.len;
+        const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
+        const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          f32x16 st = f32x16{}, dpt = f32x16{};
+          const int krow = c2 * 32 + row_perm(l32);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) st = mfma_bf16(row_operand<D>(sK, krow, c, hf), qf[c], st);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) dpt = mfma_bf16(row_operand<D>(sV, krow, c, hf), gf[c], dpt);
+          f32x16 ds;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float e = ex2(__builtin_fmaf(st[v], sl2, -lse2));
+            if (!wave_full) {
+              const int j = j0 + c2 * 32 + reg_row(v, hf);
+              const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
+              const bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+              e = ok ? e : 0.f;
+            }
+            ds[v] = e * (dpt[v] - dl);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            bf16x8 sb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sb[i] = (__bf16)ds[8 * u + i];
+            const int key0 = c2 * 32 + 16 * u + 8 * hf;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) dq[d] = mfma_bf16(tr_operand<D>(sK, key0, d, lane), sb, dq[d]);
+          }
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  if (!row_ok) return;
+  float* dqr = reinterpret_cast<float*>(a.dq.ptr) + b * a.dq.sb + (int64_t)row * a.dq.st + head * a.dq.sh;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = d * 32 + 8 * g + 4 * hf;
+      f32x4 x = *reinterpret_cast<const f32x4*>(dqr + d0);
+      x += a.scale * f32x4{dq[d][4 * g], dq[d][4 * g + 1], dq[d][4 * g + 2], dq[d][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(dqr + d0) = x;
+    }
+}
+
+// ============================================================================================
 // HBM-bound helpers
 // ============================================================================================
 
@@ -1042,8 +1641,8 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s) 
   const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (bf16) {
-    if (head_dim == 128) hipLaunchKernelGGL((fwd_kernel<128, true>), dim3(grid), dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<64, true>), dim3(grid), dim3(NT), 0, s, a);
+    if (head_dim == 128) hipLaunchKernelGGL((fwd_kernel_bf16<128>), dim3(grid), dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel_bf16<64>), dim3(grid), dim3(NT), 0, s, a);
   } else {
     if (head_dim == 128) hipLaunchKernelGGL((fwd_kernel<128, false>), dim3(grid), dim3(NT), 0, s, a);
     else hipLaunchKernelGGL((fwd_kernel<64, false>), dim3(grid), dim3(NT), 0, s, a);
@@ -1051,16 +1650,27 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool bf16, hipStream_t s) {
+hipError_t launch_bwd_fused_f32(const BwdArgs& a, int head_dim, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
-  if (bf16) {
-    if (head_dim == 128) hipLaunchKernelGGL((bwd_kernel<128, true>), dim3(grid), dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((bwd_kernel<64, true>), dim3(grid), dim3(NT), 0, s, a);
-  } else {
-    if (head_dim == 128) hipLaunchKernelGGL((bwd_kernel<128, false>), dim3(grid), dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((bwd_kernel<64, false>), dim3(grid), dim3(NT), 0, s, a);
-  }
+  if (head_dim == 128) hipLaunchKernelGGL((bwd_kernel<128, false>), dim3(grid), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((bwd_kernel<64, false>), dim3(grid), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
+  if (grid == 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(grid), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
+  if (grid == 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

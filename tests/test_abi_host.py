@@ -42,7 +42,8 @@ def test_abi_version_and_strings(ra):
     assert lib.ra_status_str(0) == b"RA_OK"
     assert lib.ra_status_str(4) == b"RA_ERR_WORKSPACE"
     assert lib.ra_kernel_name(0) == b"block_fwd"
-    assert lib.ra_kernel_name(1) == b"block_bwd"
+    assert lib.ra_kernel_name(1) == b"block_bwd_dkdv"
+    assert lib.ra_kernel_name(7) == b"block_bwd_dq"
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
