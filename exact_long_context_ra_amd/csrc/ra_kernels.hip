@@ -958,13 +958,13 @@ __device__ __forceinline__ bf16x8 row_operand(const char* tile, int row, int c, 
   return ld_bf16x8(tile + nat_off<D>(row, 2 * c + hf));
 }
 // Direct buffer->LDS copy of rows [r0, r0 + ROWS) of a [rows][D] bf16 slice into
-// a swizzled tile; wave w moves rows [w*ROWS/4, (w+1)*ROWS/4).  Rows past the
+// a swizzled tile; wave w of NWAVES moves rows [w*ROWS/NWAVES, (w+1)*ROWS/NWAVES).  Rows past the
 // slice read as zeros (buffer range check).  `w` must be wave-uniform.
-template <int D, int ROWS>
+template <int D, int ROWS, int NWAVES = 4>
 __device__ __forceinline__ void dma_tile(Rsrc rs, uint32_t st, int r0, char* tile, int w, int lane) {
   constexpr int RPI = 1024 / (2 * D);  // rows per instruction (64 lanes x 16 bytes)
   constexpr int CPR = (2 * D) / 16;    // chunks per row
-  constexpr int RPW = ROWS / 4;        // rows per wave
+  constexpr int RPW = ROWS / NWAVES;   // rows per wave
   static_assert(RPW % RPI == 0, "tile rows must split evenly over the waves");
 #pragma unroll
   for (int i = 0; i < RPW / RPI; ++i) {
@@ -1203,21 +1203,28 @@ constexpr int DQ_BK = 64;  // keys per dQ-kernel tile
 
 template <int D>
 struct DkdvB {
-  static constexpr int TILE = BQB * D * 2;
+  static constexpr int NW = 8;                    // waves: 4 key groups x 2 query halves
+  static constexpr int TILE = BQB * D * 2;        // one Q (or dO) tile
   static constexpr int OFF_DO = TILE;
-  static constexpr int OFF_ROWS = 2 * TILE;  // lse*log2e, delta, lo, hi (64 each)
+  static constexpr int OFF_ROWS = 2 * TILE;       // lse*log2e, delta, lo, hi (64 each)
   static constexpr int BUF = OFF_ROWS + 4 * BQB * 4;
-  static constexpr int LDS = 2 * BUF;
+  static constexpr int OFF_V = 2 * BUF;           // this workgroup's V tile (BWD_BK rows)
+  static constexpr int LDS = OFF_V + BWD_BK * D * 2;
 };
 
+// dK/dV kernel: 8 waves; wave (kg, qh) owns keys 32*kg.. of the workgroup's
+// 128 and query rows 32*qh.. of every 64-row query tile.  K fragments stay in
+// registers, V rows are read from an LDS tile; the two query halves of a key
+// group add their dK/dV through LDS at the end.
 template <int D>
-__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvB<D>;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w & 3, qh = w >> 2;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int kt = logical % a.n_ktiles;  // earliest (heaviest causal) key tiles first
   const int bh = logical / a.n_ktiles;
@@ -1238,19 +1245,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int k_first = kt * BWD_BK;
   const int k_last = min(a.lk, k_first + BWD_BK) - 1;
-  const int kw0 = k_first + 32 * w;
+  const int kw0 = k_first + 32 * kg;
   const int kw_last = min(k_last, kw0 + 31);
   const bool wave_has_keys = kw0 <= k_last;
   const int key = kw0 + l32;
   const bool key_ok = key <= k_last;
   const int kpos = map_pos(a.kmap, min(key, k_last));
+  const char* sV = smem + C::OFF_V;
+  dma_tile<D, BWD_BK, 8>(rv, vst, k_first, smem + C::OFF_V, w, lane);
 
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < D / 16; ++c)
     kf[c] = __builtin_bit_cast(bf16x8, bload16(rk, (uint32_t)key * kst + (16 * c + 8 * hf) * 2));
-    vf[c] = __builtin_bit_cast(bf16x8, bload16(rv, (uint32_t)key * vst + (16 * c + 8 * hf) * 2));
-  }
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
@@ -1267,11 +1274,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   if (rbeg < rend) {
     const int qt0 = rbeg / BQB, qt1 = (rend - 1) / BQB;
-    // Per-row data of a query tile travels through registers (threads 0..63).
-    RowStage rows;
+    RowStage rows;  // per-row data of the next query tile (threads 0..63)
     rows.load(a, lse_b, del_b, qt0 * BQB, tid);
-    dma_tile<D, BQB>(rq, qst, qt0 * BQB, smem, w, lane);
-    dma_tile<D, BQB>(rdo, dst, qt0 * BQB, smem + C::OFF_DO, w, lane);
+    dma_tile<D, BQB, 8>(rq, qst, qt0 * BQB, smem, w, lane);
+    dma_tile<D, BQB, 8>(rdo, dst, qt0 * BQB, smem + C::OFF_DO, w, lane);
     if (tid < BQB) {
       float* rr = reinterpret_cast<float*>(smem + C::OFF_ROWS);
       rr[tid] = rows.l;
@@ -1288,8 +1294,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       if (more) {
         char* nb = smem + (cur ^ 1) * C::BUF;
         rows.load(a, lse_b, del_b, (qt + 1) * BQB, tid);
-        dma_tile<D, BQB>(rq, qst, (qt + 1) * BQB, nb, w, lane);
-        dma_tile<D, BQB>(rdo, dst, (qt + 1) * BQB, nb + C::OFF_DO, w, lane);
+        dma_tile<D, BQB, 8>(rq, qst, (qt + 1) * BQB, nb, w, lane);
+        dma_tile<D, BQB, 8>(rdo, dst, (qt + 1) * BQB, nb + C::OFF_DO, w, lane);
       }
       const char* sQ = buf;
       const char* sDO = buf + C::OFF_DO;
@@ -1297,45 +1303,49 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const float* sDel = sLse + BQB;
       const int* sLo = reinterpret_cast<const int*>(sLse + 2 * BQB);
       const int* sHi = sLo + BQB;
-      const int nrows = min(a.lq - qt * BQB, BQB);
-      const int lo_f = sLo[0], hi_f = sHi[0], lo_l = sLo[nrows - 1], hi_l = sHi[nrows - 1];
-      const bool wave_empty = !wave_has_keys || kwmax < lo_f || kwmin > hi_l;
-      const bool wave_full = (kw0 + 32 <= a.lk) && kwmin >= lo_l && kwmax <= hi_f;
+      // this wave's 32 query rows of the tile
+      const int hr0 = qh * 32;
+      const int nrows = min(a.lq - qt * BQB - hr0, 32);
+      bool wave_empty = !wave_has_keys || nrows <= 0;
+      bool wave_full = false;
       if (!wave_empty) {
+        const int lo_f = sLo[hr0], hi_f = sHi[hr0], lo_l = sLo[hr0 + nrows - 1], hi_l = sHi[hr0 + nrows - 1];
+        wave_empty = kwmax < lo_f || kwmin > hi_l;
+        wave_full = (kw0 + 32 <= a.lk) && kwmin >= lo_l && kwmax <= hi_f;
+      }
+      if (!wave_empty) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const int qrow = hr0 + row_perm(l32);
 #pragma unroll
-        for (int qbk = 0; qbk < 2; ++qbk) {
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int qrow = qbk * 32 + row_perm(l32);
+        for (int c = 0; c < D / 16; ++c) s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), kf[c], s);
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), kf[c], s);
+        for (int c = 0; c < D / 16; ++c)
+          dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), row_operand<D>(sV, 32 * kg + l32, c, hf), dp);
+        f32x16 p, ds;
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), vf[c], dp);
-          f32x16 p, ds;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int q = qbk * 32 + reg_row(v, hf);
-            float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q]));
-            if (!wave_full) {
-              const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
-              e = ok ? e : 0.f;
-            }
-            p[v] = e;
-            ds[v] = e * (dp[v] - sDel[q]);
+        for (int v = 0; v < 16; ++v) {
+          const int q = hr0 + reg_row(v, hf);
+          float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q]));
+          if (!wave_full) {
+            const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
+            e = ok ? e : 0.f;
           }
+          p[v] = e;
+          ds[v] = e * (dp[v] - sDel[q]);
+        }
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            bf16x8 pb, sb;
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 pb, sb;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              pb[i] = (__bf16)p[8 * u + i];
-              sb[i] = (__bf16)ds[8 * u + i];
-            }
-            const int q0 = qbk * 32 + 16 * u + 8 * hf;
+          for (int i = 0; i < 8; ++i) {
+            pb[i] = (__bf16)p[8 * u + i];
+            sb[i] = (__bf16)ds[8 * u + i];
+          }
+          const int q0 = hr0 + 16 * u + 8 * hf;
 #pragma unroll
-            for (int d = 0; d < NDB; ++d) {
-              dv[d] = mfma_bf16(tr_operand<D>(sDO, q0, d, lane), pb, dv[d]);
-              dk[d] = mfma_bf16(tr_operand<D>(sQ, q0, d, lane), sb, dk[d]);
-            }
+          for (int d = 0; d < NDB; ++d) {
+            dv[d] = mfma_bf16(tr_operand<D>(sDO, q0, d, lane), pb, dv[d]);
+            dk[d] = mfma_bf16(tr_operand<D>(sQ, q0, d, lane), sb, dk[d]);
           }
         }
       }
@@ -1350,22 +1360,60 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       __syncthreads();
     }
   }
+  wait_vmem();  // the V tile DMA when no query tile was visited
+  __syncthreads();
 
-  if (!key_ok) return;
+  // Add the two query halves of each key group: waves qh = 1 park dK^T / dV^T
+  // in LDS (reusing the query buffers), waves qh = 0 add and write out.
+  float* red = reinterpret_cast<float*>(smem);  // 4 key groups x 64 lanes x 16*NDB floats
+  constexpr int PER = 16 * NDB;
   float* dkr = reinterpret_cast<float*>(a.dk.ptr) + b * a.dk.sb + (int64_t)key * a.dk.st + head * a.dk.sh;
   float* dvr = reinterpret_cast<float*>(a.dv.ptr) + b * a.dv.sb + (int64_t)key * a.dv.st + head * a.dv.sh;
+  float* slot = red + (kg * 64 + lane) * PER;
+  // pass 0: dK (scaled), pass 1: dV
+  if (qh == 1) {
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = d * 32 + 8 * g + 4 * hf;
-      f32x4 x = *reinterpret_cast<const f32x4*>(dkr + d0);
-      f32x4 y = *reinterpret_cast<const f32x4*>(dvr + d0);
-      x += a.scale * f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]};
-      y += f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]};
-      *reinterpret_cast<f32x4*>(dkr + d0) = x;
-      *reinterpret_cast<f32x4*>(dvr + d0) = y;
-    }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(slot + 16 * d + 4 * g) =
+            f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]};
+  }
+  __syncthreads();
+  if (qh == 0 && key_ok) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = d * 32 + 8 * g + 4 * hf;
+        const f32x4 other = *reinterpret_cast<const f32x4*>(slot + 16 * d + 4 * g);
+        f32x4 x = *reinterpret_cast<const f32x4*>(dkr + d0);
+        x += a.scale * (f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]} + other);
+        *reinterpret_cast<f32x4*>(dkr + d0) = x;
+      }
+  }
+  __syncthreads();
+  if (qh == 1) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(slot + 16 * d + 4 * g) =
+            f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]};
+  }
+  __syncthreads();
+  if (qh == 0 && key_ok) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = d * 32 + 8 * g + 4 * hf;
+        const f32x4 other = *reinterpret_cast<const f32x4*>(slot + 16 * d + 4 * g);
+        f32x4 y = *reinterpret_cast<const f32x4*>(dvr + d0);
+        y += f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]} + other;
+        *reinterpret_cast<f32x4*>(dvr + d0) = y;
+      }
+  }
 }
 
 template <int D>
@@ -1661,8 +1709,8 @@ hipError_t launch_bwd_fused_f32(const BwdArgs& a, int head_dim, hipStream_t s) {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(grid), dim3(NT), 0, s, a);
+  if (head_dim == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
