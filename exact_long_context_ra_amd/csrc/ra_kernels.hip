@@ -977,6 +977,17 @@ __device__ __forceinline__ void dma_tile(Rsrc rs, uint32_t st, int r0, char* til
 }
 // Wait for this wave's outstanding global/buffer loads (including buffer->LDS).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (they complete in issue order), leaving the newest N in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// Direct buffer->LDS copy of 64 consecutive fp32 values (one per lane).
+__device__ __forceinline__ void dma_f32x64(Rsrc rs, int first, char* dst, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (uint32_t)(first + lane) * 4, 0, 0, 0);
+}
 
 // ============================================================================================
 // bf16 forward: tiles of 64 keys, K and V DMA'd one tile ahead into the other
@@ -1206,16 +1217,22 @@ struct DkdvB {
   static constexpr int NW = 8;                    // waves: 4 key groups x 2 query halves
   static constexpr int TILE = BQB * D * 2;        // one Q (or dO) tile
   static constexpr int OFF_DO = TILE;
-  static constexpr int OFF_ROWS = 2 * TILE;       // lse*log2e, delta, lo, hi (64 each)
-  static constexpr int BUF = OFF_ROWS + 4 * BQB * 4;
-  static constexpr int OFF_V = 2 * BUF;           // this workgroup's V tile (BWD_BK rows)
+  static constexpr int OFF_LSE = 2 * TILE;        // 64 lse values (natural log, as given)
+  static constexpr int OFF_DEL = OFF_LSE + BQB * 4;
+  static constexpr int BUF = OFF_DEL + BQB * 4;
+  static constexpr int NBUF = 2;                  // query tiles are fetched one ahead
+  static constexpr int OFF_K = NBUF * BUF;        // this workgroup's K tile (BWD_BK rows)
+  static constexpr int OFF_V = OFF_K + BWD_BK * D * 2;  // and its V tile
   static constexpr int LDS = OFF_V + BWD_BK * D * 2;
 };
 
 // dK/dV kernel: 8 waves; wave (kg, qh) owns keys 32*kg.. of the workgroup's
-// 128 and query rows 32*qh.. of every 64-row query tile.  K fragments stay in
-// registers, V rows are read from an LDS tile; the two query halves of a key
-// group add their dK/dV through LDS at the end.
+// 128 and query rows 32*qh.. of every 64-row query tile.  K and V rows are
+// read from LDS tiles; query tiles (with their lse and delta) are DMA'd one
+// tile ahead into two LDS buffers.  Visibility is
+// tested per key lane: a query position qp sees this lane's key iff qp lies in
+// the key's column interval (col_bounds), so no per-row lookups are needed.
+// The two query halves of a key group add their dK/dV through LDS at the end.
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvB<D>;
@@ -1238,10 +1255,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
   const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, 2, D));
   const Rsrc rdo = make_rsrc(dobase, slice_bytes(a.lq, a.dout.st, 2, D));
+  const Rsrc rlse = make_rsrc(a.lse + ((int64_t)b * a.heads + head) * a.lq, (uint32_t)a.lq * 4);
+  const Rsrc rdel = make_rsrc(a.delta + ((int64_t)b * a.heads + head) * a.lq, (uint32_t)a.lq * 4);
   const uint32_t qst = (uint32_t)(a.q.st * 2), kst = (uint32_t)(a.k.st * 2);
   const uint32_t vst = (uint32_t)(a.v.st * 2), dst = (uint32_t)(a.dout.st * 2);
-  const float* lse_b = a.lse + ((int64_t)b * a.heads + head) * a.lq;
-  const float* del_b = a.delta + ((int64_t)b * a.heads + head) * a.lq;
 
   const int k_first = kt * BWD_BK;
   const int k_last = min(a.lk, k_first + BWD_BK) - 1;
@@ -1250,14 +1267,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bool wave_has_keys = kw0 <= k_last;
   const int key = kw0 + l32;
   const bool key_ok = key <= k_last;
-  const int kpos = map_pos(a.kmap, min(key, k_last));
-  const char* sV = smem + C::OFF_V;
-  dma_tile<D, BWD_BK, 8>(rv, vst, k_first, smem + C::OFF_V, w, lane);
+  const Bounds cb = col_bounds(a.mask, map_pos(a.kmap, min(key, k_last)));       // this lane's key
+  const Bounds cbf = col_bounds(a.mask, map_pos(a.kmap, min(kw0, k_last)));      // wave's first key
+  const Bounds cbl = col_bounds(a.mask, map_pos(a.kmap, kw_last));               // wave's last key
 
-  bf16x8 kf[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    kf[c] = __builtin_bit_cast(bf16x8, bload16(rk, (uint32_t)key * kst + (16 * c + 8 * hf) * 2));
+  dma_tile<D, BWD_BK, 8>(rk, kst, k_first, smem + C::OFF_K, w, lane);
+  dma_tile<D, BWD_BK, 8>(rv, vst, k_first, smem + C::OFF_V, w, lane);
+  const char* sK = smem + C::OFF_K;
+  const char* sV = smem + C::OFF_V;
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
@@ -1269,55 +1286,52 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const Bounds cl = col_bounds(a.mask, map_pos(a.kmap, k_last));
   const int rbeg = first_ge(a.qmap, cf.lo);
   const int rend = min(a.lq, last_le(a.qmap, cl.hi) + 1);
-  const int kwmin = map_pos(a.kmap, min(kw0, k_last)), kwmax = map_pos(a.kmap, kw_last);
   const float sl2 = a.scale_log2;
+
+  auto issue = [&](int qtile, int slot) {
+    char* nb = smem + slot * C::BUF;
+    const int r0 = qtile * BQB;
+    dma_tile<D, BQB, 8>(rq, qst, r0, nb, w, lane);
+    dma_tile<D, BQB, 8>(rdo, dst, r0, nb + C::OFF_DO, w, lane);
+    if (w == 0) dma_f32x64(rlse, r0, nb + C::OFF_LSE, lane);
+    if (w == 1) dma_f32x64(rdel, r0, nb + C::OFF_DEL, lane);
+  };
 
   if (rbeg < rend) {
     const int qt0 = rbeg / BQB, qt1 = (rend - 1) / BQB;
-    RowStage rows;  // per-row data of the next query tile (threads 0..63)
-    rows.load(a, lse_b, del_b, qt0 * BQB, tid);
-    dma_tile<D, BQB, 8>(rq, qst, qt0 * BQB, smem, w, lane);
-    dma_tile<D, BQB, 8>(rdo, dst, qt0 * BQB, smem + C::OFF_DO, w, lane);
-    if (tid < BQB) {
-      float* rr = reinterpret_cast<float*>(smem + C::OFF_ROWS);
-      rr[tid] = rows.l;
-      rr[BQB + tid] = rows.dl;
-      reinterpret_cast<int*>(rr)[2 * BQB + tid] = rows.lo;
-      reinterpret_cast<int*>(rr)[3 * BQB + tid] = rows.hi;
-    }
+    issue(qt0, 0);
     wait_vmem();
     __syncthreads();
     for (int qt = qt0; qt <= qt1; ++qt) {
-      const int cur = (qt - qt0) & 1;
-      const char* buf = smem + cur * C::BUF;
-      const bool more = qt < qt1;
-      if (more) {
-        char* nb = smem + (cur ^ 1) * C::BUF;
-        rows.load(a, lse_b, del_b, (qt + 1) * BQB, tid);
-        dma_tile<D, BQB, 8>(rq, qst, (qt + 1) * BQB, nb, w, lane);
-        dma_tile<D, BQB, 8>(rdo, dst, (qt + 1) * BQB, nb + C::OFF_DO, w, lane);
-      }
+      const int i = qt - qt0;
+      const char* buf = smem + (i & 1) * C::BUF;
+      if (qt + 1 <= qt1) issue(qt + 1, (i + 1) & 1);
       const char* sQ = buf;
       const char* sDO = buf + C::OFF_DO;
-      const float* sLse = reinterpret_cast<const float*>(buf + C::OFF_ROWS);
-      const float* sDel = sLse + BQB;
-      const int* sLo = reinterpret_cast<const int*>(sLse + 2 * BQB);
-      const int* sHi = sLo + BQB;
+      const float* sLse = reinterpret_cast<const float*>(buf + C::OFF_LSE);
+      const float* sDel = reinterpret_cast<const float*>(buf + C::OFF_DEL);
       // this wave's 32 query rows of the tile
-      const int hr0 = qh * 32;
-      const int nrows = min(a.lq - qt * BQB - hr0, 32);
-      bool wave_empty = !wave_has_keys || nrows <= 0;
+      const int rw0 = qt * BQB + qh * 32;
+      const int rwl = min(a.lq - 1, rw0 + 31);
+      bool wave_empty = !wave_has_keys || rw0 > rwl;
       bool wave_full = false;
+      int qp0 = 0, qstr = 1;
       if (!wave_empty) {
-        const int lo_f = sLo[hr0], hi_f = sHi[hr0], lo_l = sLo[hr0 + nrows - 1], hi_l = sHi[hr0 + nrows - 1];
-        wave_empty = kwmax < lo_f || kwmin > hi_l;
-        wave_full = (kw0 + 32 <= a.lk) && kwmin >= lo_l && kwmax <= hi_f;
+        const int qfirst = map_pos(a.qmap, rw0), qlast = map_pos(a.qmap, rwl);
+        wave_empty = qlast < cbf.lo || qfirst > cbl.hi;
+        wave_full = (kw0 + 32 <= a.lk) && (rw0 + 32 <= a.lq) && qfirst >= cbl.lo && qlast <= cbf.hi;
+        const bool in0 = rw0 < a.qmap.s0.len;
+        const bool one_seg = a.qmap.nseg < 2 || in0 == (rwl < a.qmap.s0.len);
+        qp0 = qfirst;
+        qstr = one_seg ? (in0 ? a.qmap.s0.stride : a.qmap.s1.stride) : 0;  // 0: look each row up
       }
       if (!wave_empty) {
+        const int hr0 = qh * 32;
         f32x16 s = f32x16{}, dp = f32x16{};
         const int qrow = hr0 + row_perm(l32);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), kf[c], s);
+        for (int c = 0; c < D / 16; ++c)
+          s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), row_operand<D>(sK, 32 * kg + l32, c, hf), s);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
           dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), row_operand<D>(sV, 32 * kg + l32, c, hf), dp);
@@ -1325,9 +1339,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int q = hr0 + reg_row(v, hf);
-          float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q]));
+          float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q] * LOG2E));
           if (!wave_full) {
-            const bool ok = key_ok && kpos >= sLo[q] && kpos <= sHi[q];
+            const int r = qt * BQB + q;
+            const int qp = qstr ? qp0 + (q - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
+            const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
             e = ok ? e : 0.f;
           }
           p[v] = e;
@@ -1337,9 +1353,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int u = 0; u < 2; ++u) {
           bf16x8 pb, sb;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            pb[i] = (__bf16)p[8 * u + i];
-            sb[i] = (__bf16)ds[8 * u + i];
+          for (int i2 = 0; i2 < 8; ++i2) {
+            pb[i2] = (__bf16)p[8 * u + i2];
+            sb[i2] = (__bf16)ds[8 * u + i2];
           }
           const int q0 = hr0 + 16 * u + 8 * hf;
 #pragma unroll
@@ -1349,18 +1365,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
           }
         }
       }
-      if (more && tid < BQB) {
-        float* rr = reinterpret_cast<float*>(smem + (cur ^ 1) * C::BUF + C::OFF_ROWS);
-        rr[tid] = rows.l;
-        rr[BQB + tid] = rows.dl;
-        reinterpret_cast<int*>(rr)[2 * BQB + tid] = rows.lo;
-        reinterpret_cast<int*>(rr)[3 * BQB + tid] = rows.hi;
-      }
       wait_vmem();
       __syncthreads();
     }
   }
-  wait_vmem();  // the V tile DMA when no query tile was visited
+  wait_vmem();  // the K/V tile DMA when no query tile was visited
   __syncthreads();
 
   // Add the two query halves of each key group: waves qh = 1 park dK^T / dV^T
