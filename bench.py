@@ -42,6 +42,25 @@ WORKLOADS = {
 HEADS, HEAD_DIM = 32, 128
 
 
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/hbm_traffic.txt (rocprofv3
+    FETCH_SIZE/WRITE_SIZE, copy-calibrated), or None when the kernels changed
+    since the counters were taken (source hash mismatch) or none were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    src = os.path.join(ROOT, "exact_long_context_ra_amd", "csrc", "ra_kernels.hip")
+    try:
+        lines = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    rec = {ln[0]: ln[1:] for ln in lines}
+    if rec.get("kernel_source_sha256", [None])[0] != cur or kernel not in rec:
+        return None
+    vals = dict(zip(rec[kernel][::2], rec[kernel][1::2]))
+    return int(vals["fetch_bytes"]) + int(vals["write_bytes"])
+
+
 def visible_pairs(qpos: np.ndarray, kpos: np.ndarray, cu) -> int:
     """Exact causal visible pairs of sorted positions (varlen: same sequence)."""
     kpos = np.sort(kpos)
@@ -210,8 +229,9 @@ def main():
     dk = per_kernel[dom]
     if dom in per_pair and dk["ms"] > 0:
         achieved = dk["flops"] / (dk["ms"] / 1e3) / 1e12
+        traffic = profiled_traffic(dom) if args.workload == "zigzag" else None
         roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": dom,
+                    "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": dom,
                     "avg_launch_ms": dk["ms"] / max(1, dk["launches"]), "launches": dk["launches"]}
     else:
         roofline = {"bound": "hbm", "achieved": None, "peak": 8000.0, "unit": "GB/s", "frac": None,
