@@ -9,3 +9,7 @@ from .api import (  # noqa: F401
     ring_workspace_bytes,
 )
 from ._lib import RAError, lib  # noqa: F401
+from .functional import (  # noqa: F401
+    gathered_share_attn, ring_attn_func, ring_attn_kvpacked_func, ring_attn_qkvpacked_func,
+    ring_attn_varlen_func,
+)

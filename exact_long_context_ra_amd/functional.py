@@ -1,0 +1,164 @@
+"""Autograd-facing forms of the virtual ring, mirroring the reference API's
+function family ("Ring Flash Attention" README, function list: ring /
+zigzag ring / stripe functions, each with plain, kv-packed and qkv-packed
+forms, and a varlen form taking one cu_seqlens).
+
+Every function here computes on ONE GPU: the global sequence is laid out
+into the N ranks' local chunks by the library's layout positions, every
+rank's share runs through ra_ring_fwd / ra_ring_bwd (the virtual ring), and
+the per-rank results are scattered back to global token order.  Packed
+inputs are accepted as strided views: the ring forms gather them into
+rank-major K/V rings (one copy, as a real ring's send buffers would be), and
+the block step (`gathered_share_attn`, `api.block_attn_fwd`) reads strided
+views in place.  Gradients are exact softmax-attention gradients (the
+backward recomputes P from the saved lse).
+
+The llama3-style context-parallel share (SourcePulse summary of the
+reference, "How It Works" / "Highlighted Details": gather all K/V, then a
+rank attends its local queries against them) is `gathered_share_attn`: one
+block step over the whole gathered K/V with the rank's global positions.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+from . import api
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _positions(layout: str, S: int, world: int, device):
+    torch = _torch()
+    return [torch.from_numpy(api.layout_positions(layout, S, world, r)).to(device) for r in range(world)]
+
+
+class _VirtualRing:
+    """Shared forward/backward of the virtual ring over global [b, S, h, d] tensors."""
+
+    @staticmethod
+    def forward(q, k, v, layout, world, causal, cu_seqlens, scale):
+        torch = _torch()
+        b, S, h, d = q.shape
+        idx = _positions(layout, S, world, q.device)
+        k_ring = torch.stack([k.index_select(1, i) for i in idx]).contiguous()
+        v_ring = torch.stack([v.index_select(1, i) for i in idx]).contiguous()
+        out = torch.empty((b, S, h, d), device=q.device, dtype=q.dtype)
+        lse = torch.empty((b, h, S), device=q.device, dtype=torch.float32)
+        outs, lses = [], []
+        for r in range(world):
+            ql = q.index_select(1, idx[r]).contiguous()
+            o32, l, _ = api.ring_fwd(layout, world, r, ql, k_ring, v_ring, causal=causal, cu_seqlens=cu_seqlens,
+                                     scale=scale)
+            outs.append(o32)
+            lses.append(l)
+            out.index_copy_(1, idx[r], o32.to(q.dtype))
+            lse.index_copy_(2, idx[r], l)
+        return out, lse, (idx, k_ring, v_ring, outs, lses)
+
+    @staticmethod
+    def backward(q, dout, layout, world, causal, cu_seqlens, scale, saved):
+        torch = _torch()
+        idx, k_ring, v_ring, outs, lses = saved
+        b, S, h, d = q.shape
+        dq = torch.empty((b, S, h, d), device=q.device, dtype=torch.float32)
+        dk_ring = torch.zeros(k_ring.shape, device=q.device, dtype=torch.float32)
+        dv_ring = torch.zeros(v_ring.shape, device=q.device, dtype=torch.float32)
+        for r in range(world):
+            ql = q.index_select(1, idx[r]).contiguous()
+            dol = dout.index_select(1, idx[r]).contiguous().to(q.dtype)
+            dqr, _, _ = api.ring_bwd(layout, world, r, ql, k_ring, v_ring, outs[r], lses[r], dol, causal=causal,
+                                     cu_seqlens=cu_seqlens, scale=scale, dk_ring=dk_ring, dv_ring=dv_ring)
+            dq.index_copy_(1, idx[r], dqr)
+        dk = torch.empty((b, S, h, d), device=q.device, dtype=torch.float32)
+        dv = torch.empty((b, S, h, d), device=q.device, dtype=torch.float32)
+        for r in range(world):
+            dk.index_copy_(1, idx[r], dk_ring[r])
+            dv.index_copy_(1, idx[r], dv_ring[r])
+        return dq, dk, dv
+
+
+def _make_function():
+    torch = _torch()
+
+    class RingAttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, layout, world, causal, cu_seqlens, scale):
+            out, lse, saved = _VirtualRing.forward(q.detach(), k.detach(), v.detach(), layout, world, causal,
+                                                   cu_seqlens, scale)
+            ctx.saved = saved
+            ctx.args = (layout, world, causal, cu_seqlens, scale)
+            ctx.save_for_backward(q.detach())
+            ctx.dtypes = (q.dtype, k.dtype, v.dtype)
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            (q,) = ctx.saved_tensors
+            layout, world, causal, cu_seqlens, scale = ctx.args
+            dq, dk, dv = _VirtualRing.backward(q, dout.contiguous(), layout, world, causal, cu_seqlens, scale,
+                                               ctx.saved)
+            ctx.saved = None
+            qd, kd, vd = ctx.dtypes
+            return dq.to(qd), dk.to(kd), dv.to(vd), None, None, None, None, None
+
+    return RingAttentionFn
+
+
+_FN = None
+
+
+def ring_attn_func(q, k, v, *, layout: str = "zigzag", world: int = 8, causal: bool = True,
+                   softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """Exact attention of global [b, S, h, d] q/k/v through an N-rank virtual ring.
+
+    Differentiable with respect to q, k and v.  Returns out (q.dtype) and, when
+    asked, the fp32 lse [b, h, S]."""
+    global _FN
+    if _FN is None:
+        _FN = _make_function()
+    out, lse = _FN.apply(q, k, v, layout, world, causal, None, softmax_scale)
+    return (out, lse) if return_lse else out
+
+
+def ring_attn_varlen_func(q, k, v, cu_seqlens: Sequence[int], *, layout: str = "contiguous", world: int = 8,
+                          causal: bool = True, softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """Packed variable-length form: q/k/v are [1, T, h, d] (or [T, h, d]) holding
+    several sequences back to back, delimited by ONE cu_seqlens shared by q and
+    k/v (int32 global offsets, first 0, last T)."""
+    global _FN
+    if _FN is None:
+        _FN = _make_function()
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+    out, lse = _FN.apply(q, k, v, layout, world, causal, cu_seqlens, softmax_scale)
+    if squeeze:
+        out = out.squeeze(0)
+    return (out, lse) if return_lse else out
+
+
+def ring_attn_kvpacked_func(q, kv, **kw):
+    """kv: [b, S, 2, h, d] (K then V along dim 2), taken as strided views."""
+    return ring_attn_func(q, kv[:, :, 0], kv[:, :, 1], **kw)
+
+
+def ring_attn_qkvpacked_func(qkv, **kw):
+    """qkv: [b, S, 3, h, d] (Q, K, V along dim 2), taken as strided views."""
+    return ring_attn_func(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], **kw)
+
+
+def gathered_share_attn(q_local, k_all, v_all, *, layout: str = "contiguous", world: int = 8, rank: int = 0,
+                        causal: bool = True, cu_seqlens=None, softmax_scale: Optional[float] = None):
+    """One rank's share when all K/V have been gathered (llama3-style context
+    parallelism): q_local [b, S/N, h, d] of `rank` in `layout` attends to the
+    whole k_all/v_all [b, S, h, d] in global order, as a single block step.
+    Returns (out fp32, lse fp32)."""
+    S = k_all.shape[1]
+    qm = api.layout_posmap(layout, S, world, rank)
+    km = api.posmap([(0, 1, S)])
+    return api.block_attn_fwd(q_local, k_all, v_all, qm, km, seq_len=S, causal=causal, cu_seqlens=cu_seqlens,
+                              scale=softmax_scale)
