@@ -218,10 +218,11 @@ def main():
         agg["ms"] += ms
     # Matrix-product FLOPs each kernel executes over the timed region, per
     # visible pair and head: forward QK^T + PV = 4*D; the dK/dV kernel
-    # recomputes S and dP and forms dV, dK = 8*D; the dQ kernel recomputes S
-    # and dP and forms dQ = 6*D.  (The metric above counts the backward as
-    # 10*D per pair, the five products of the textbook gradient.)
-    per_pair = {"block_fwd": 4.0, "block_bwd_dkdv": 8.0, "block_bwd_dq": 6.0}
+    # recomputes S and dP and forms dV, dK = 8*D; the dQ kernel either reads the
+    # dS the dK/dV kernel stored and forms dQ = 2*D, or (small workspace)
+    # recomputes S and dP as well = 6*D.  (The metric above counts the backward
+    # as 10*D per pair, the five products of the textbook gradient.)
+    per_pair = {"block_fwd": 4.0, "block_bwd_dkdv": 8.0, "block_bwd_dq_ds": 2.0, "block_bwd_dq": 6.0}
     for name, f in per_pair.items():
         per_kernel.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0})["flops"] = (
             f * D * H * total_pairs * args.steps)

@@ -75,8 +75,9 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = C.c_int
-        L.ra_ring_workspace_bytes.argtypes = [P(ra_problem), C.c_int32, C.c_int32]
-        L.ra_ring_workspace_bytes.restype = C.c_size_t
+        for name in ("ra_ring_workspace_bytes", "ra_ring_workspace_min_bytes"):
+            getattr(L, name).argtypes = [P(ra_problem), C.c_int32, C.c_int32]
+            getattr(L, name).restype = C.c_size_t
         for name in ("ra_status_str", "ra_kernel_name"):
             getattr(L, name).restype = C.c_char_p
         L.ra_status_str.argtypes = [C.c_int]

@@ -209,17 +209,22 @@ def ring_fwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, *, cau
     return out, lse, out_lowp
 
 
-def ring_workspace_bytes(layout: str, world: int, q_local, causal: bool = True) -> int:
+def ring_workspace_bytes(layout: str, world: int, q_local, causal: bool = True, minimal: bool = False) -> int:
+    """Workspace bytes ring_bwd uses: its fastest path (stored dS for bf16), or with
+    ``minimal`` the least it accepts (dQ then recomputes S and dP)."""
     b, L, h, d = q_local.shape
     p = _problem(q_local, h, d, L * world, causal, None, _Cu(None, None))
-    return int(lib().ra_ring_workspace_bytes(C.byref(p), _layout_id(layout), world))
+    fn = lib().ra_ring_workspace_min_bytes if minimal else lib().ra_ring_workspace_bytes
+    return int(fn(C.byref(p), _layout_id(layout), world))
 
 
 def ring_bwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, out, lse, dout, *,
              causal: bool = True, cu_seqlens=None, scale: Optional[float] = None,
-             dq=None, dk_ring=None, dv_ring=None, workspace=None):
+             dq=None, dk_ring=None, dv_ring=None, workspace=None, store_ds: bool = True):
     """Backward of rank ``rank``'s share.  dq is overwritten; dk_ring/dv_ring (fp32) are accumulated
-    (allocated zeroed when not given).  Returns (dq, dk_ring, dv_ring)."""
+    (allocated zeroed when not given).  ``workspace`` (uint8 device tensor) is allocated when not
+    given: of ring_workspace_bytes() with ``store_ds`` (dQ from the stored dS), else of the
+    minimal size (dQ recomputes S and dP).  Returns (dq, dk_ring, dv_ring)."""
     torch = _torch()
     b, L, h, d = q_local.shape
     S = L * world
@@ -232,7 +237,8 @@ def ring_bwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, out, l
         dv_ring = torch.zeros((world, b, L, h, d), device=dev, dtype=torch.float32)
     cu = _Cu(cu_seqlens, dev)
     p = _problem(q_local, h, d, S, causal, scale, cu)
-    need = int(lib().ra_ring_workspace_bytes(C.byref(p), _layout_id(layout), world))
+    fn = lib().ra_ring_workspace_bytes if store_ds else lib().ra_ring_workspace_min_bytes
+    need = int(fn(C.byref(p), _layout_id(layout), world))
     if workspace is None:
         workspace = torch.empty(max(need, 256), device=dev, dtype=torch.uint8)
     kt, srank = _t5(k_ring)

@@ -303,6 +303,7 @@ const char* ra_kernel_name(int32_t id) {
     case K_FWD: return "block_fwd";
     case K_BWD: return "block_bwd_dkdv";
     case K_BWD_DQ: return "block_bwd_dq";
+    case K_BWD_DQ_DS: return "block_bwd_dq_ds";
     case K_MERGE: return "lse_merge";
     case K_PREP: return "bwd_preprocess";
     case K_FILL: return "fill";
@@ -458,11 +459,15 @@ ra_status ra_bwd_preprocess(const ra_problem* prob, int64_t lq, ra_tensor out, r
   return RA_OK;
 }
 
-// One backward block step: bf16 runs the dK/dV and dQ kernels, fp32 the fused kernel.
+// One backward block step: bf16 runs the dK/dV kernel and then dQ, from the dS
+// it stored when a.dsT is set, else by recomputing S and dP; fp32 runs the fused kernel.
 static ra_status launch_bwd_step(const BwdArgs& a, int head_dim, bool bf16, int step, hipStream_t s) {
   if (bf16) {
     RA_HIP(timed(K_BWD, step, s, [&] { return launch_bwd_dkdv(a, head_dim, s); }));
-    RA_HIP(timed(K_BWD_DQ, step, s, [&] { return launch_bwd_dq(a, head_dim, s); }));
+    if (a.dsT)
+      RA_HIP(timed(K_BWD_DQ_DS, step, s, [&] { return launch_bwd_dq_ds(a, head_dim, s); }));
+    else
+      RA_HIP(timed(K_BWD_DQ, step, s, [&] { return launch_bwd_dq(a, head_dim, s); }));
   } else {
     RA_HIP(timed(K_BWD, step, s, [&] { return launch_bwd_fused_f32(a, head_dim, s); }));
   }
@@ -592,13 +597,34 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   return RA_OK;
 }
 
-size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
+// Workspace of ra_ring_bwd: delta [b, h, L] fp32 (rounded up to 256 bytes), then
+// for bf16 the dS^T buffer: per (b, h) a blocked [keys][query rows] slice of
+// round_up(L, 128) keys (whole dK/dV key tiles) by ds_ld = round_up(L, 128) rows
+// (whole dQ row tiles), bf16.
+static int64_t ds_ld_of(int64_t L) { return (L + FWD_BQ - 1) / FWD_BQ * FWD_BQ; }
+
+size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
   if (check_problem(prob) != RA_OK || world < 1) return 0;
   ra_posmap m;
   if (make_posmap(layout, prob->seq_len, world, 0, &m) != RA_OK) return 0;
   const int64_t L = prob->seq_len / world;
   const size_t bytes = (size_t)prob->batch * prob->heads * L * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
+}
+
+// dS^T bytes for the stored-dS path, or 0 where that path does not apply (fp32,
+// or one (b, h) slice too large for the kernels' 32-bit buffer offsets).
+static size_t ds_bytes(const ra_problem* prob, int64_t L) {
+  if (prob->dtype != RA_DTYPE_BF16 || L == 0) return 0;
+  const int64_t slice = (L + BWD_BK - 1) / BWD_BK * BWD_BK * ds_ld_of(L) * 2;
+  if (slice >= ((int64_t)1 << 31)) return 0;
+  return (size_t)prob->batch * prob->heads * (size_t)slice;
+}
+
+size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
+  const size_t base = ra_ring_workspace_min_bytes(prob, layout, world);
+  if (base == 0) return 0;
+  return base + ds_bytes(prob, prob->seq_len / world);
 }
 
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
@@ -623,10 +649,12 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
            "stride_rank must be >= 0 and keep 16-byte alignment");
   RA_CHECK(stride_rank_grad >= 0 && stride_rank_grad % 4 == 0, RA_ERR_INVALID_ARG,
            "stride_rank_grad must be >= 0 and keep 16-byte alignment");
-  const size_t need = ra_ring_workspace_bytes(prob, layout, world);
+  const size_t need = ra_ring_workspace_min_bytes(prob, layout, world);
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
            "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  const size_t dsb = ds_bytes(prob, L);
+  uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
 
   ra_posmap qmap;
   make_posmap(layout, prob->seq_len, world, rank, &qmap);
@@ -656,6 +684,8 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     bwd_args(prob, q_local, L, qmap, offset_rd(k_ring, src * stride_rank, esz),
              offset_rd(v_ring, src * stride_rank, esz), L, kmap, dout, lse, delta, dqw,
              offset_wr(dk_ring, src * stride_rank_grad, 4), offset_wr(dv_ring, src * stride_rank_grad, 4), &a);
+    a.dsT = dsT;
+    a.ds_ld = ds_ld_of(L);
     ra_status st2 = launch_bwd_step(a, prob->head_dim, bf16, step, s);
     if (st2 != RA_OK) return st2;
   }

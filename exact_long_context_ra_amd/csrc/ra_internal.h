@@ -59,7 +59,11 @@ struct BwdArgs {
   float scale;         // softmax_scale
   float scale_log2;    // softmax_scale * log2(e)
   int32_t n_ktiles;    // key tiles (dK/dV and fused kernels)
-  int32_t n_qtiles;    // query tiles (dQ kernel)
+  int32_t n_qtiles;    // query tiles (dQ kernels)
+  // bf16 dS^T [b][h][lk][ds_ld] (query rows contiguous), or null.  Written by
+  // the dK/dV kernel when set; read by the dQ-from-dS kernel.
+  uint16_t* dsT;
+  int64_t ds_ld;
 };
 
 struct MergeArgs {
@@ -92,8 +96,9 @@ enum KernelId : int32_t {
   K_FILL = 4,
   K_CAST = 5,
   K_ZERO = 6,
-  K_BWD_DQ = 7,  // bf16 dQ kernel
-  K_COUNT = 8
+  K_BWD_DQ = 7,     // bf16 dQ kernel (recomputes S and dP)
+  K_BWD_DQ_DS = 8,  // bf16 dQ kernel reading the stored dS
+  K_COUNT = 9
 };
 
 // Tile sizes shared by planner and kernels.
@@ -105,6 +110,7 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_bwd_fused_f32(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fill(const FillArgs& a, hipStream_t s);

@@ -1212,6 +1212,32 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
 
 constexpr int DQ_BK = 64;  // keys per dQ-kernel tile
 
+// Blocked dS^T layout of one (batch, head) slice: blocks of 32 keys x 16
+// query rows (1 KiB), each stored key-major with the key's 16 rows contiguous;
+// blocks ordered by 32-key block, then by 16-row block (ds_ld / 16 of them).
+// Element offset of (key, row):
+__device__ __forceinline__ int64_t ds_offset(int key, int row, int64_t ds_ld) {
+  return ((int64_t)(key >> 5) * (ds_ld >> 4) + (row >> 4)) * 512 + (key & 31) * 16 + (row & 15);
+}
+// Elements of one slice: keys padded to whole dK/dV key tiles.
+__device__ __forceinline__ int64_t ds_slice_elems(int lk, int64_t ds_ld) {
+  return (int64_t)((lk + BWD_BK - 1) / BWD_BK * BWD_BK) * ds_ld;
+}
+
+// Query tiles (BQB rows) that the dK/dV kernel visits for its key tile kt
+// (BWD_BK keys): [q0, q1], empty when q0 > q1.  Both the dK/dV kernel and the
+// dQ-from-dS kernel take the range from here, so they agree exactly.
+__device__ __forceinline__ void dkdv_query_tiles(const BwdArgs& a, int kt, int& q0, int& q1) {
+  const int k_first = kt * BWD_BK;
+  const int k_last = min(a.lk, k_first + BWD_BK) - 1;
+  const Bounds cf = col_bounds(a.mask, map_pos(a.kmap, k_first));
+  const Bounds cl = col_bounds(a.mask, map_pos(a.kmap, k_last));
+  const int rbeg = first_ge(a.qmap, cf.lo);
+  const int rend = min(a.lq, last_le(a.qmap, cl.hi) + 1);
+  q0 = rbeg / BQB;
+  q1 = rbeg < rend ? (rend - 1) / BQB : q0 - 1;
+}
+
 template <int D>
 struct DkdvB {
   static constexpr int NW = 8;                    // waves: 4 key groups x 2 query halves
@@ -1221,9 +1247,12 @@ struct DkdvB {
   static constexpr int OFF_DEL = OFF_LSE + BQB * 4;
   static constexpr int BUF = OFF_DEL + BQB * 4;
   static constexpr int NBUF = 2;                  // query tiles are fetched one ahead
-  static constexpr int OFF_K = NBUF * BUF;        // this workgroup's K tile (BWD_BK rows)
-  static constexpr int OFF_V = OFF_K + BWD_BK * D * 2;  // and its V tile
-  static constexpr int LDS = OFF_V + BWD_BK * D * 2;
+  // The K and V tiles come first, so that a V address is the matching K
+  // address plus an immediate offset that fits the LDS instruction.
+  static constexpr int OFF_K = 0;                 // this workgroup's K tile (BWD_BK rows)
+  static constexpr int OFF_V = BWD_BK * D * 2;    // and its V tile
+  static constexpr int OFF_BUF = 2 * BWD_BK * D * 2;
+  static constexpr int LDS = OFF_BUF + NBUF * BUF;
 };
 
 // dK/dV kernel: 8 waves; wave (kg, qh) owns keys 32*kg.. of the workgroup's
@@ -1267,6 +1296,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const bool wave_has_keys = kw0 <= k_last;
   const int key = kw0 + l32;
   const bool key_ok = key <= k_last;
+  // Optional dS^T output in the blocked layout of ds_offset(): one wave's
+  // 32 keys x 16 rows are one contiguous KiB, so each store instruction writes
+  // whole cache lines.  Through a buffer descriptor over this (batch, head)
+  // slice, of size 0 when there is no dS^T buffer, so that every store is then
+  // dropped (the store itself stays unconditional: a branch around it costs
+  // the loop registers).  Every visited (query tile, key) block is written,
+  // zeros where nothing is visible, so the dQ kernel reads only written data.
+  const bool ds_on = a.dsT != nullptr;
+  const int64_t ds_slice = ds_slice_elems(a.lk, a.ds_ld);
+  const Rsrc rds = make_rsrc(ds_on ? a.dsT + (int64_t)(b * a.heads + head) * ds_slice : a.dsT,
+                             ds_on ? (uint32_t)(ds_slice * 2) : 0u);
+  const uint32_t ds_voff = (uint32_t)(ds_offset(l32, 8 * hf, 0) * 2);   // this lane's 16 bytes of a block
+  const int ds_kblock = kt * (BWD_BK / 32) + kg;                         // this wave's 32-key block
   const Bounds cb = col_bounds(a.mask, map_pos(a.kmap, min(key, k_last)));       // this lane's key
   const Bounds cbf = col_bounds(a.mask, map_pos(a.kmap, min(kw0, k_last)));      // wave's first key
   const Bounds cbl = col_bounds(a.mask, map_pos(a.kmap, kw_last));               // wave's last key
@@ -1282,14 +1324,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dv[d] = f32x16{};
   }
 
-  const Bounds cf = col_bounds(a.mask, map_pos(a.kmap, k_first));
-  const Bounds cl = col_bounds(a.mask, map_pos(a.kmap, k_last));
-  const int rbeg = first_ge(a.qmap, cf.lo);
-  const int rend = min(a.lq, last_le(a.qmap, cl.hi) + 1);
+  int qt0, qt1;
+  dkdv_query_tiles(a, kt, qt0, qt1);
   const float sl2 = a.scale_log2;
 
+  // Per-lane offsets of the transposed reads within a query tile: rows
+  // 32*qh + 8*hf + (j >> 2) + 4*hi at column 32*d + 16*g1 + 4*(j & 3) (j = lane
+  // mod 16, g1 = bit 4 of the lane).  The rows 16*u further down sit 16*u*2*D
+  // bytes further (the swizzle depends on the row modulo 16 only), so u is an
+  // immediate offset rather than another register per read.
+  int offT[NDB][2];
+  {
+    const int j = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int colb = 2 * (32 * d + 16 * g1 + 4 * (j & 3));
+        offT[d][hi] = nat_off<D>(32 * qh + 8 * hf + (j >> 2) + 4 * hi, colb >> 4) + (colb & 15);
+      }
+  }
+  auto tr_op = [&](const char* tile, int u, int d) {
+    const u32x2 lo = tr16(tile + u * 16 * 2 * D + offT[d][0]);
+    const u32x2 hi = tr16(tile + u * 16 * 2 * D + offT[d][1]);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+
   auto issue = [&](int qtile, int slot) {
-    char* nb = smem + slot * C::BUF;
+    char* nb = smem + C::OFF_BUF + slot * C::BUF;
     const int r0 = qtile * BQB;
     dma_tile<D, BQB, 8>(rq, qst, r0, nb, w, lane);
     dma_tile<D, BQB, 8>(rdo, dst, r0, nb + C::OFF_DO, w, lane);
@@ -1297,14 +1359,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (w == 1) dma_f32x64(rdel, r0, nb + C::OFF_DEL, lane);
   };
 
-  if (rbeg < rend) {
-    const int qt0 = rbeg / BQB, qt1 = (rend - 1) / BQB;
+  // dS^T of a tile is stored at the start of the next one: the wait at the end
+  // of a tile covers every memory operation of the wave (stores included), and
+  // a store issued a whole tile earlier has completed by then.  A pending store
+  // with nothing to write gets an offset past any buffer (2^31: the descriptor
+  // is smaller, and adding the scalar offset does not wrap) and is dropped.
+  constexpr uint32_t kNoStore = 0x80000000u;
+  bf16x8 pend[2] = {zero_bf16x8(), zero_bf16x8()};
+  uint32_t pend_voff = kNoStore, pend_soff = 0;
+  auto flush = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pend[u]), rds, pend_voff,
+                                             pend_soff + 1024 * u, 0);
+  };
+
+  if (qt0 <= qt1) {
     issue(qt0, 0);
     wait_vmem();
     __syncthreads();
     for (int qt = qt0; qt <= qt1; ++qt) {
       const int i = qt - qt0;
-      const char* buf = smem + (i & 1) * C::BUF;
+      const char* buf = smem + C::OFF_BUF + (i & 1) * C::BUF;
+      flush();
       if (qt + 1 <= qt1) issue(qt + 1, (i + 1) & 1);
       const char* sQ = buf;
       const char* sDO = buf + C::OFF_DO;
@@ -1335,45 +1412,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
           dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), row_operand<D>(sV, 32 * kg + l32, c, hf), dp);
-        f32x16 p, ds;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int q = hr0 + reg_row(v, hf);
-          float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q] * LOG2E));
-          if (!wave_full) {
-            const int r = qt * BQB + q;
-            const int qp = qstr ? qp0 + (q - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
-            const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
-            e = ok ? e : 0.f;
-          }
-          p[v] = e;
-          ds[v] = e * (dp[v] - sDel[q]);
-        }
+        // P and dS per half u of this lane's 16 rows, packed to bf16 as made.
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           bf16x8 pb, sb;
 #pragma unroll
           for (int i2 = 0; i2 < 8; ++i2) {
-            pb[i2] = (__bf16)p[8 * u + i2];
-            sb[i2] = (__bf16)ds[8 * u + i2];
+            const int v = 8 * u + i2;
+            const int q = hr0 + reg_row(v, hf);
+            float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q] * LOG2E));
+            if (!wave_full) {
+              int hq = 8 * hf;
+              asm volatile("" : "+v"(hq));
+              const int qm = hr0 + 16 * u + hq + i2;
+              const int r = qt * BQB + qm;
+              const int qp = qstr ? qp0 + (qm - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
+              const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
+              e = ok ? e : 0.f;
+            }
+            pb[i2] = (__bf16)e;
+            sb[i2] = (__bf16)(e * (dp[v] - sDel[q]));
           }
-          const int q0 = hr0 + 16 * u + 8 * hf;
+          pend[u] = sb;
 #pragma unroll
           for (int d = 0; d < NDB; ++d) {
-            dv[d] = mfma_bf16(tr_operand<D>(sDO, q0, d, lane), pb, dv[d]);
-            dk[d] = mfma_bf16(tr_operand<D>(sQ, q0, d, lane), sb, dk[d]);
+            dv[d] = mfma_bf16(tr_op(sDO, u, d), pb, dv[d]);
+            dk[d] = mfma_bf16(tr_op(sQ, u, d), sb, dk[d]);
           }
         }
       }
+      // This tile's block of dS^T is stored with the next tile; blocks that
+      // nothing in them sees are stored as zeros, rows past lq not at all.
+      if (wave_empty) {
+        pend[0] = zero_bf16x8();
+        pend[1] = zero_bf16x8();
+      }
+      pend_voff = rw0 <= rwl ? ds_voff : kNoStore;
+      pend_soff = (uint32_t)(ds_offset(32 * ds_kblock, rw0, a.ds_ld) * 2);
       wait_vmem();
       __syncthreads();
     }
+    flush();
   }
   wait_vmem();  // the K/V tile DMA when no query tile was visited
   __syncthreads();
 
   // Add the two query halves of each key group: waves qh = 1 park dK^T / dV^T
-  // in LDS (reusing the query buffers), waves qh = 0 add and write out.
+  // in LDS (reusing the K/V tiles), waves qh = 0 add and write out.
   float* red = reinterpret_cast<float*>(smem);  // 4 key groups x 64 lanes x 16*NDB floats
   constexpr int PER = 16 * NDB;
   float* dkr = reinterpret_cast<float*>(a.dk.ptr) + b * a.dk.sb + (int64_t)key * a.dk.st + head * a.dk.sh;
@@ -1563,6 +1648,121 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
+// dQ from the stored dS^T: a workgroup owns 128 query rows (32 per wave) and
+// walks the 64-key tiles they can see: dQ^T += K^T dS^T, both operands
+// through transposed reads of natural LDS tiles (the K tile, and the dS^T
+// tile [64 keys][128 rows]), DMA'd one tile ahead.  A wave skips a key tile
+// whose dK/dV workgroup did not visit the wave's query tile: nothing there is
+// visible and that block of dS^T was not written.
+template <int D>
+struct DqsB {
+  static constexpr int KT = DQ_BK * D * 2;       // K tile
+  static constexpr int ST = DQ_BK * FWD_BQ * 2;  // dS^T tile: 64 keys x 128 query rows
+  static constexpr int BUF = KT + ST;
+  static constexpr int LDS = 2 * BUF;
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_ds_kernel(BwdArgs a) {
+  using C = DqsB<D>;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;
+  const int bh = logical / a.n_qtiles;
+  const int head = bh % a.heads, b = bh / a.heads;
+
+  const int r_first = qt * FWD_BQ;
+  const int r_last = min(a.lq, r_first + FWD_BQ) - 1;
+  const int w_first = r_first + 32 * w;
+  const bool wave_has_rows = w_first <= r_last;
+  const int row = w_first + l32;
+  const bool row_ok = row <= r_last;
+  const int my_qtile = w_first / BQB;  // the dK/dV kernel's query tile holding this wave's rows
+
+  const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * 2;
+  const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
+  const uint32_t kst = (uint32_t)(a.k.st * 2);
+  // This (batch, head) slice of dS^T (blocked layout, see ds_offset).
+  const int64_t ds_elems = ds_slice_elems(a.lk, a.ds_ld);
+  const Rsrc rs = make_rsrc(a.dsT + (int64_t)(b * a.heads + head) * ds_elems, (uint32_t)(ds_elems * 2));
+  // DMA of the dS^T tile [64 keys][128 query rows] into a natural swizzled LDS
+  // tile: wave w moves tile rows (keys) 16*w .. 16*w+15, four per instruction;
+  // lane l fills LDS position l mod 16 of key 16*w + 4*i + l/16, which holds
+  // the chunk of 8 query rows c = position ^ swz(key).  Per instruction this
+  // gathers 8 runs of 128 contiguous bytes.
+  auto dma_ds = [&](int jt, char* tile) {
+#pragma unroll
+    for (int i = 0; i < DQ_BK / 16; ++i) {
+      const int kr = 16 * w + 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ swz<128>(kr);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void*)(tile + (16 * w + 4 * i) * 256), 16,
+          (uint32_t)(ds_offset(jt * DQ_BK + kr, r_first + 8 * c, a.ds_ld) * 2), 0, 0, 0);
+    }
+  };
+
+  const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
+  const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
+  const int kbeg = first_ge(a.kmap, wg_f.lo);
+  const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
+
+  if (kbeg < kend) {
+    const int jt0 = kbeg / DQ_BK, jt1 = (kend - 1) / DQ_BK;
+    auto issue = [&](int jt, char* buf) {
+      dma_tile<D, DQ_BK>(rk, kst, jt * DQ_BK, buf, w, lane);
+      dma_ds(jt, buf + C::KT);
+    };
+    issue(jt0, smem);
+    wait_vmem();
+    __syncthreads();
+    int cov_tile = -1;
+    bool covered = false;
+    for (int jt = jt0; jt <= jt1; ++jt) {
+      const int cur = (jt - jt0) & 1;
+      const char* sK = smem + cur * C::BUF;
+      const char* sS = sK + C::KT;
+      if (jt < jt1) issue(jt + 1, smem + (cur ^ 1) * C::BUF);
+      const int kt = jt * DQ_BK / BWD_BK;
+      if (kt != cov_tile) {
+        int q0, q1;
+        dkdv_query_tiles(a, kt, q0, q1);
+        covered = my_qtile >= q0 && my_qtile <= q1;
+        cov_tile = kt;
+      }
+      if (wave_has_rows && covered) {
+#pragma unroll
+        for (int ks = 0; ks < DQ_BK / 16; ++ks) {
+          const bf16x8 sop = tr_operand<128>(sS, 16 * ks + 8 * hf, w, lane);
+#pragma unroll
+          for (int d = 0; d < NDB; ++d) acc[d] = mfma_bf16(tr_operand<D>(sK, 16 * ks + 8 * hf, d, lane), sop, acc[d]);
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  if (!row_ok) return;
+  float* dqr = reinterpret_cast<float*>(a.dq.ptr) + b * a.dq.sb + (int64_t)row * a.dq.st + head * a.dq.sh;
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = d * 32 + 8 * g + 4 * hf;
+      f32x4 x = *reinterpret_cast<const f32x4*>(dqr + d0);
+      x += a.scale * f32x4{acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(dqr + d0) = x;
+    }
+}
+
 // ============================================================================================
 // HBM-bound helpers
 // ============================================================================================
@@ -1720,6 +1920,14 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(512), 0, s, a);
   else hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
+  if (grid == 0) return hipSuccess;
+  if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_ds_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_ds_kernel<64>), dim3(grid), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
 #define RA_MAX_TIMED_LAUNCHES 65536
 
 typedef enum {
@@ -159,15 +159,25 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
  *  dk_ring, dv_ring: fp32, block n at ptr + n*stride_rank_grad elements, each
  *  [b, S/N, h, d]; ACCUMULATED (+=) with this rank's contribution, so that running
  *  every rank into the same buffers yields the full gradients.
- *  workspace: device memory of at least ra_ring_workspace_bytes() bytes. */
+ *  workspace: device memory, 16-byte aligned, of at least ra_ring_workspace_min_bytes()
+ *  bytes.  It holds delta = rowsum(dO * O) (the preprocessing step of the backward in
+ *  "Ring Flash Attention", zhuzilin/ring-flash-attention README) and, for bf16 when it
+ *  reaches ra_ring_workspace_bytes(), the bf16 dS^T of the current step: the dK/dV
+ *  kernel then stores dS and dQ = dS K is one product per pair instead of a recompute
+ *  of S, P and dP.  With less than that, dQ is computed by the recompute kernel. */
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
                       ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
                       ra_tensor out, const float* lse, ra_tensor dout,
                       ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace ra_ring_bwd needs (0 on invalid input). */
+/* Bytes of device workspace for ra_ring_bwd's fastest path (0 on invalid input):
+ * delta (b*h*L fp32) and, for bf16, dS^T (b*h*round_up(L, 128)^2 bf16), L = S/N.
+ * Never smaller than ra_ring_workspace_min_bytes(). */
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world);
+
+/* Smallest workspace ra_ring_bwd accepts (delta only; 0 on invalid input). */
+size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world);
 
 /* ---- utilities ---------------------------------------------------------------------------- */
 

@@ -38,12 +38,13 @@ def test_header_symbols_exported(ra):
 
 def test_abi_version_and_strings(ra):
     lib = ra.lib()
-    assert lib.ra_abi_version() == 1
+    assert lib.ra_abi_version() == 2
     assert lib.ra_status_str(0) == b"RA_OK"
     assert lib.ra_status_str(4) == b"RA_ERR_WORKSPACE"
     assert lib.ra_kernel_name(0) == b"block_fwd"
     assert lib.ra_kernel_name(1) == b"block_bwd_dkdv"
     assert lib.ra_kernel_name(7) == b"block_bwd_dq"
+    assert lib.ra_kernel_name(8) == b"block_bwd_dq_ds"
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
@@ -148,8 +149,12 @@ def test_workspace_validation(ra):
     from exact_long_context_ra_amd._lib import RA_ERR_WORKSPACE
     lib = ra.lib()
     p = _problem(ra)
-    need = lib.ra_ring_workspace_bytes(C.byref(p), 0, 4)
-    assert need == 256  # batch*heads*L*4 = 1*2*16*4 = 128, rounded up to 256
+    need = lib.ra_ring_workspace_min_bytes(C.byref(p), 0, 4)
+    assert need == 256  # delta: batch*heads*L*4 = 1*2*16*4 = 128, rounded up to 256
+    full = lib.ra_ring_workspace_bytes(C.byref(p), 0, 4)
+    assert full == need + 1 * 2 * 128 * 128 * 2  # + bf16 dS^T: b*h*round_up(L, 128)^2
+    p32 = _problem(ra, dtype=0)
+    assert lib.ra_ring_workspace_bytes(C.byref(p32), 0, 4) == lib.ra_ring_workspace_min_bytes(C.byref(p32), 0, 4)
     st = lib.ra_ring_bwd(C.byref(p), 0, 4, 0, _t(), _t(), _t(), 0, _t(), 4096, _t(), _t(), _t(), _t(), 0,
                          4096, need - 1, None)
     assert st == RA_ERR_WORKSPACE

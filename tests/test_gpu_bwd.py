@@ -82,14 +82,21 @@ RING_BWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", RING_BWD_CASES, ids=lambda c: "-".join(str(x) for x in c))
-def test_ring_bwd(case):
+# bf16 runs both dQ paths: from the dS the dK/dV kernel stores (full workspace)
+# and by recomputing S and dP (minimal workspace); fp32 has one path.
+RING_BWD_RUNS = [(c, True) for c in RING_BWD_CASES] + [(c, False) for c in RING_BWD_CASES if c[5] == "bf16"]
+
+
+@pytest.mark.parametrize("case,store_ds", RING_BWD_RUNS,
+                         ids=lambda c: "-".join(str(x) for x in c) if isinstance(c, tuple) else
+                         ("ds" if c else "recompute"))
+def test_ring_bwd(case, store_ds):
     """Every rank runs fwd then bwd into shared dK/dV ring buffers: per-rank dQ
     and the summed dK/dV must equal the full-sequence gradients."""
     import torch
     ra = _ra()
     layout, S, N, H, D, dt, cu = case
-    log(f"ring_bwd {case}")
+    log(f"ring_bwd {case} store_ds={store_ds}")
     if cu == "varlen":
         lengths = [1, 200, 1, 129, 300]
         lengths.append(S - sum(lengths))
@@ -110,7 +117,7 @@ def test_ring_bwd(case):
         dol = do.index_select(1, idx[r]).contiguous()
         out, lse, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True, cu_seqlens=cu)
         dq, _, _ = ra.ring_bwd(layout, N, r, ql, kr, vr, out, lse, dol, causal=True, cu_seqlens=cu,
-                               dk_ring=dk_ring, dv_ring=dv_ring)
+                               dk_ring=dk_ring, dv_ring=dv_ring, store_ds=store_ds)
         torch.cuda.synchronize()
         opos = oracle.layout_positions(layout, S, N, r)
         check_grad(f64(dq), gq[:, opos], bf, what=f"dq r={r}")
