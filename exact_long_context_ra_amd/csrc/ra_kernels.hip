@@ -928,9 +928,18 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Chunk swizzle of a natural [rows][D] bf16 LDS tile: 16-byte chunk c of row r
+// sits at chunk position c ^ swz(r).  For D = 128 it is a linear map of the row
+// bits 0..3 (row bit b flips the position bits of mask {6, 10, 8, 13}[b]),
+// chosen so that on gfx950's 64-bank LDS both access patterns of the kernels
+// are free of bank conflicts: 16-byte row reads of 32 rows (row_perm order),
+// served 16 lanes at a time, and the transposed 8-byte reads of 8-row column
+// strips, served 32 lanes at a time (checked with the SQ_LDS_BANK_CONFLICT
+// counter).  It depends on the row modulo 16 only.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+  if constexpr (D == 128)
+    return (6 & -(r & 1)) ^ (10 & -((r >> 1) & 1)) ^ (8 & -((r >> 2) & 1)) ^ (13 & -((r >> 3) & 1));
   else return (r >> 1) & 7;
 }
 // Byte offset of 16-byte chunk `chunk` of row `row` in a swizzled [rows][D] bf16 tile.
