@@ -1413,34 +1413,52 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       if (!wave_empty) {
         const int hr0 = qh * 32;
+        // S = Q K^T and dP = dO V^T, the two chains interleaved per k-step.
         f32x16 s = f32x16{}, dp = f32x16{};
         const int qrow = hr0 + row_perm(l32);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
+        for (int c = 0; c < D / 16; ++c) {
           s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), row_operand<D>(sK, 32 * kg + l32, c, hf), s);
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
           dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), row_operand<D>(sV, 32 * kg + l32, c, hf), dp);
-        // P and dS per half u of this lane's 16 rows, packed to bf16 as made.
+        }
+        // P and dS per half u of this lane's 16 rows (rows hr0 + 16u + 8hf + i2),
+        // packed to bf16 as they are made; lse (to base 2) and delta of the
+        // 8 rows come as two 16-byte reads each.  Fully visible blocks take a
+        // copy of the loop without the visibility test.
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
+          const int qb = hr0 + 16 * u + 8 * hf;
+          const f32x4 la = *reinterpret_cast<const f32x4*>(sLse + qb);
+          const f32x4 lb = *reinterpret_cast<const f32x4*>(sLse + qb + 4);
+          const f32x4 da = *reinterpret_cast<const f32x4*>(sDel + qb);
+          const f32x4 db = *reinterpret_cast<const f32x4*>(sDel + qb + 4);
           bf16x8 pb, sb;
+          if (wave_full) {
 #pragma unroll
-          for (int i2 = 0; i2 < 8; ++i2) {
-            const int v = 8 * u + i2;
-            const int q = hr0 + reg_row(v, hf);
-            float e = ex2(__builtin_fmaf(s[v], sl2, -sLse[q] * LOG2E));
-            if (!wave_full) {
-              int hq = 8 * hf;
-              asm volatile("" : "+v"(hq));
+            for (int i2 = 0; i2 < 8; ++i2) {
+              const int v = 8 * u + i2;
+              const float lse = i2 < 4 ? la[i2] : lb[i2 - 4];
+              const float del = i2 < 4 ? da[i2] : db[i2 - 4];
+              const float e = ex2(__builtin_fmaf(s[v], sl2, -lse * LOG2E));
+              pb[i2] = (__bf16)e;
+              sb[i2] = (__bf16)(e * (dp[v] - del));
+            }
+          } else {
+            int hq = 8 * hf;
+            asm volatile("" : "+v"(hq));  // keeps the 16 row indices from being precomputed
+#pragma unroll
+            for (int i2 = 0; i2 < 8; ++i2) {
+              const int v = 8 * u + i2;
+              const float lse = i2 < 4 ? la[i2] : lb[i2 - 4];
+              const float del = i2 < 4 ? da[i2] : db[i2 - 4];
               const int qm = hr0 + 16 * u + hq + i2;
               const int r = qt * BQB + qm;
               const int qp = qstr ? qp0 + (qm - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
               const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
-              e = ok ? e : 0.f;
+              const float e = ok ? ex2(__builtin_fmaf(s[v], sl2, -lse * LOG2E)) : 0.f;
+              pb[i2] = (__bf16)e;
+              sb[i2] = (__bf16)(e * (dp[v] - del));
             }
-            pb[i2] = (__bf16)e;
-            sb[i2] = (__bf16)(e * (dp[v] - sDel[q]));
           }
           pend[u] = sb;
 #pragma unroll
