@@ -1022,14 +1022,13 @@ __device__ __forceinline__ void fwd_tile_bf16(const FwdArgs& a, int j0, const ch
   const bool wave_full = (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
   const float sl2 = a.scale_log2;
 
-  f32x16 st[2];
+  // S^T for the two 32-key halves of the tile, the two MFMA chains interleaved.
+  f32x16 st[2] = {f32x16{}, f32x16{}};
+  const int row = row_perm(l32);
 #pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) {
-    f32x16 acc = f32x16{};
-    const int row = c2 * 32 + row_perm(l32);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) acc = mfma_bf16(row_operand<D>(sK, row, c, hf), qf[c], acc);
-    st[c2] = acc;
+  for (int c = 0; c < D / 16; ++c) {
+    st[0] = mfma_bf16(row_operand<D>(sK, row, c, hf), qf[c], st[0]);
+    st[1] = mfma_bf16(row_operand<D>(sK, 32 + row, c, hf), qf[c], st[1]);
   }
   if (!wave_full) {
     const bool in0 = j0 < a.kmap.s0.len;
@@ -1374,13 +1373,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // with nothing to write gets an offset past any buffer (2^31: the descriptor
   // is smaller, and adding the scalar offset does not wrap) and is dropped.
   constexpr uint32_t kNoStore = 0x80000000u;
+  constexpr int kNonTemporal = 2;  // cache-policy bit: dS^T streams out, no reuse before the dQ kernel
   bf16x8 pend[2] = {zero_bf16x8(), zero_bf16x8()};
   uint32_t pend_voff = kNoStore, pend_soff = 0;
   auto flush = [&]() {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pend[u]), rds, pend_voff,
-                                             pend_soff + 1024 * u, 0);
+                                             pend_soff + 1024 * u, kNonTemporal);
   };
 
   if (qt0 <= qt1) {
