@@ -53,7 +53,7 @@ from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-LAYOUTS = ("contiguous", "zigzag", "stripe")
+LAYOUTS = ("contiguous", "zigzag", "stripe", "zigzag_varlen", "stripe_varlen")
 
 # Work per row-block of the score matrix: at most this many float64 scores.
 _BLOCK_ELEMS = 1 << 24
@@ -64,16 +64,31 @@ _BLOCK_ELEMS = 1 << 24
 # [RFA] function list; [STRIPE] abstract)
 # ---------------------------------------------------------------------------
 
-def layout_positions(layout: str, seq_len: int, world: int, rank: int) -> np.ndarray:
+def layout_positions(layout: str, seq_len: int, world: int, rank: int, cu_seqlens=None) -> np.ndarray:
     """Global token position of each local token of ``rank`` (local order).
 
     contiguous: rank r owns the r-th of N equal consecutive chunks.
     zigzag:     2N equal chunks; rank r owns chunk r then chunk 2N-1-r.
     stripe:     token t belongs to rank t mod N (a "block size" of one token).
+    zigzag_varlen / stripe_varlen: the same layout applied to every packed
+        sequence of ``cu_seqlens`` on its own ([RFA] function list: the zigzag
+        and stripe forms of the varlen function); rank r's tokens are its part
+        of sequence 0, then its part of sequence 1, and so on.  Every sequence
+        length must split evenly (2N chunks for zigzag, N for stripe).
+    ``cu_seqlens`` is used by the per-sequence layouts only.
     """
     S, N, r = int(seq_len), int(world), int(rank)
     if not (0 <= r < N):
         raise ValueError("rank out of range")
+    if layout in ("zigzag_varlen", "stripe_varlen"):
+        if cu_seqlens is None:
+            raise ValueError(f"{layout} needs cu_seqlens")
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        if cu[0] != 0 or cu[-1] != S or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must rise from 0 to seq_len")
+        base = layout[: -len("_varlen")]
+        parts = [cu[i] + layout_positions(base, int(cu[i + 1] - cu[i]), N, r) for i in range(len(cu) - 1)]
+        return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
     if layout == "contiguous":
         if S % N:
             raise ValueError("seq_len must be divisible by world")
@@ -258,7 +273,7 @@ def ring_forward(layout: str, world: int, rank: int, q_local, k_ring, v_ring,
     q_local = _f64(q_local)
     B, L, H, Dh = q_local.shape
     S = L * world
-    qpos = layout_positions(layout, S, world, rank)
+    qpos = layout_positions(layout, S, world, rank, cu_seqlens)
     srcs = ring_sources(world, rank)
     if steps is None:
         steps = range(world)
@@ -269,7 +284,7 @@ def ring_forward(layout: str, world: int, rank: int, q_local, k_ring, v_ring,
         out, lse = _f64(init[0]).copy(), _f64(init[1]).copy()
     for s in steps:
         src = srcs[s]
-        kpos = layout_positions(layout, S, world, src)
+        kpos = layout_positions(layout, S, world, src, cu_seqlens)
         ob, lb = attention(q_local, k_ring[src], v_ring[src], qpos, kpos, causal, cu_seqlens, scale)
         out, lse = lse_merge(out, lse, ob, lb)
     return out, lse
@@ -338,12 +353,12 @@ def ring_backward(layout: str, world: int, rank: int, q_local, k_ring, v_ring,
     q_local = _f64(q_local)
     B, L, H, Dh = q_local.shape
     S = L * world
-    qpos = layout_positions(layout, S, world, rank)
+    qpos = layout_positions(layout, S, world, rank, cu_seqlens)
     dq = np.zeros_like(q_local)
     dk_ring = np.zeros(np.shape(k_ring), dtype=np.float64)
     dv_ring = np.zeros(np.shape(v_ring), dtype=np.float64)
     for src in ring_sources(world, rank):
-        kpos = layout_positions(layout, S, world, src)
+        kpos = layout_positions(layout, S, world, src, cu_seqlens)
         a, b_, c = attention_backward(q_local, k_ring[src], v_ring[src], out, lse, dout,
                                       qpos, kpos, causal, cu_seqlens, scale)
         dq += a
@@ -356,11 +371,11 @@ def ring_backward(layout: str, world: int, rank: int, q_local, k_ring, v_ring,
 # Helpers for tests: gathering a global tensor into the ring's block order
 # ---------------------------------------------------------------------------
 
-def to_ring(x_global, layout: str, world: int) -> np.ndarray:
+def to_ring(x_global, layout: str, world: int, cu_seqlens=None) -> np.ndarray:
     """[b, S, h, d] -> [N, b, S/N, h, d] by the oracle's own layout positions."""
     x_global = np.asarray(x_global)
     S = x_global.shape[1]
-    return np.stack([x_global[:, layout_positions(layout, S, world, r)] for r in range(world)])
+    return np.stack([x_global[:, layout_positions(layout, S, world, r, cu_seqlens)] for r in range(world)])
 
 
 def varlen_lengths_to_cu(lengths: Sequence[int]) -> np.ndarray:

@@ -339,6 +339,52 @@ def check_layouts(orc):
     assert len(vals) == 1
 
 
+def check_varlen_layout_golden(orc):
+    with open(os.path.join(GOLDEN, "varlen_layout_examples.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            layout, S, N, r = parts[0], int(parts[1]), int(parts[2]), int(parts[3])
+            cu = [int(x) for x in parts[4].split(",")]
+            want = [int(x) for x in parts[5:]]
+            got = orc.layout_positions(layout, S, N, r, cu)
+            assert list(got) == want, f"{layout} S={S} N={N} r={r} cu={cu}: {list(got)}"
+
+
+def check_varlen_layouts(orc):
+    """Per-sequence layouts: a permutation of the stream; with one sequence the
+    plain layout; each rank's tokens of a sequence stay inside it, in order;
+    causal pair counts per rank equal the per-sequence closed forms summed,
+    and zigzag keeps them equal across ranks."""
+    for base, mult in (("zigzag", 2), ("stripe", 1)):
+        layout = base + "_varlen"
+        for N in (1, 2, 3, 4):
+            S = 8 * mult * N
+            for r in range(N):
+                assert np.array_equal(orc.layout_positions(layout, S, N, r, [0, S]),
+                                      orc.layout_positions(base, S, N, r))
+            for cu in ([0, S], [0, mult * N, S], [0, mult * N * 3, mult * N * 3, S],
+                       [0, mult * N, 2 * mult * N, 5 * mult * N, S]):
+                allpos = np.concatenate([orc.layout_positions(layout, S, N, r, cu) for r in range(N)])
+                assert np.array_equal(np.sort(allpos), np.arange(S)), f"{layout} {cu} not a permutation"
+                counts = []
+                for r in range(N):
+                    qpos = orc.layout_positions(layout, S, N, r, cu)
+                    assert np.all(np.diff(qpos) > 0), "local order must follow global order"
+                    sid = np.searchsorted(cu, qpos, side="right") - 1
+                    per = np.bincount(sid, minlength=len(cu) - 1)
+                    assert np.array_equal(per, np.diff(cu) // N), f"{layout} {cu} r={r}: tokens per sequence"
+                    got = sum(orc.count_pairs(qpos, orc.layout_positions(layout, S, N, src, cu), True, cu)
+                              for src in range(N))
+                    want = sum(closed_form_pairs(base, n, N, r) for n in np.diff(cu) if n > 0)
+                    assert got == want, f"{layout} {cu} r={r}: pairs {got} != {want}"
+                    counts.append(got)
+                if base == "zigzag":
+                    assert len(set(counts)) == 1, f"zigzag_varlen {cu}: unbalanced {counts}"
+
+
 def check_stripe_rule(orc):
     """Stripe step mask in local indices: key b visible to query a iff
     b <= a when src <= r, and b <= a-1 when src > r (from pos = index*N + rank)."""
@@ -367,15 +413,17 @@ def check_ring_union(orc):
         ("zigzag", 48, 3, True, None), ("stripe", 24, 2, False, None),
         ("contiguous", 32, 4, True, [0, 5, 6, 19, 32]),
         ("stripe", 32, 4, True, [0, 9, 32]),
+        ("zigzag_varlen", 48, 3, True, [0, 6, 6, 30, 48]),
+        ("stripe_varlen", 36, 4, True, [0, 4, 24, 36]),
     ]:
         qg, kg, vg = _rand(rng, B, S, H, D), _rand(rng, B, S, H, D), _rand(rng, B, S, H, D)
         full_o, full_l = brute_attention(qg, kg, vg, np.arange(S), np.arange(S), causal, cu,
                                          1 / math.sqrt(D))
-        kr, vr = orc.to_ring(kg, layout, N), orc.to_ring(vg, layout, N)
+        kr, vr = orc.to_ring(kg, layout, N, cu), orc.to_ring(vg, layout, N, cu)
         got_o = np.zeros_like(full_o)
         got_l = np.zeros_like(full_l)
         for r in range(N):
-            pos = orc.layout_positions(layout, S, N, r)
+            pos = orc.layout_positions(layout, S, N, r, cu)
             o, l = orc.ring_forward(layout, N, r, qg[:, pos], kr, vr, causal, cu)
             got_o[:, pos] = o
             got_l[:, :, pos] = l
@@ -383,7 +431,7 @@ def check_ring_union(orc):
         _close(got_l, full_l, what=f"ring union lse {layout} N={N} cu={cu}")
         # resume: steps [0, s) then [s, N) equals all steps
         r = N - 1
-        pos = orc.layout_positions(layout, S, N, r)
+        pos = orc.layout_positions(layout, S, N, r, cu)
         s = N // 2
         first = orc.ring_forward(layout, N, r, qg[:, pos], kr, vr, causal, cu, steps=range(s))
         second = orc.ring_forward(layout, N, r, qg[:, pos], kr, vr, causal, cu,
@@ -496,28 +544,31 @@ def check_ring_backward_union(orc):
     rng = np.random.default_rng(20)
     B, H, D = 1, 2, 4
     for layout, S, N, cu in [("contiguous", 24, 3, None), ("zigzag", 32, 4, None),
-                             ("stripe", 24, 4, None), ("contiguous", 32, 4, [0, 3, 20, 32])]:
+                             ("stripe", 24, 4, None), ("contiguous", 32, 4, [0, 3, 20, 32]),
+                             ("zigzag_varlen", 36, 3, [0, 12, 12, 36]),
+                             ("stripe_varlen", 28, 4, [0, 8, 28])]:
         qg, kg, vg, dog = (_rand(rng, B, S, H, D) for _ in range(4))
         pos = np.arange(S)
         fo, fl = orc.attention(qg, kg, vg, pos, pos, True, cu)
         fdq, fdk, fdv = orc.attention_backward(qg, kg, vg, fo, fl, dog, pos, pos, True, cu)
-        kr, vr = orc.to_ring(kg, layout, N), orc.to_ring(vg, layout, N)
+        kr, vr = orc.to_ring(kg, layout, N, cu), orc.to_ring(vg, layout, N, cu)
         dk_sum = np.zeros_like(kr)
         dv_sum = np.zeros_like(vr)
         for r in range(N):
-            p = orc.layout_positions(layout, S, N, r)
+            p = orc.layout_positions(layout, S, N, r, cu)
             o, l = orc.ring_forward(layout, N, r, qg[:, p], kr, vr, True, cu)
             dq, dkr, dvr = orc.ring_backward(layout, N, r, qg[:, p], kr, vr, o, l, dog[:, p], True, cu)
             _close(dq, fdq[:, p], what=f"ring bwd dq {layout}")
             dk_sum += dkr
             dv_sum += dvr
-        _close(dk_sum, orc.to_ring(fdk, layout, N), what=f"ring bwd dk {layout}")
-        _close(dv_sum, orc.to_ring(fdv, layout, N), what=f"ring bwd dv {layout}")
+        _close(dk_sum, orc.to_ring(fdk, layout, N, cu), what=f"ring bwd dk {layout}")
+        _close(dv_sum, orc.to_ring(fdv, layout, N, cu), what=f"ring bwd dv {layout}")
 
 
 ALL_CHECKS = [
     check_brute_force, check_torch_sdpa, check_closed_forms, check_hand_example,
-    check_split_merge, check_layout_golden, check_layouts, check_stripe_rule,
+    check_split_merge, check_layout_golden, check_layouts, check_varlen_layout_golden,
+    check_varlen_layouts, check_stripe_rule,
     check_ring_union, check_varlen_independent, check_backward_fd,
     check_backward_autograd, check_backward_invariants, check_ring_backward_union,
 ]

@@ -31,6 +31,10 @@ MUTANTS = {
     "bwd_dq_no_scale": ("dq[b, i0:i1, h, :] = scale * (ds @ k[b, :, h, :])",
                         "dq[b, i0:i1, h, :] = ds @ k[b, :, h, :]"),
     "bwd_dv_uses_ds": ("dv[b, :, h, :] += p.T @ do", "dv[b, :, h, :] += ds.T @ do"),
+    "varlen_layout_no_offset": ("parts = [cu[i] + layout_positions(base",
+                                "parts = [0 * cu[i] + layout_positions(base"),
+    "varlen_layout_whole_stream": ("base = layout[: -len(\"_varlen\")]",
+                                   "return layout_positions(layout[: -len(\"_varlen\")], S, N, r)"),
     "bwd_p_uses_m": ("np.exp(s - np.where(live, row_lse, 0.0)[:, None]), 0.0)",
                      "np.exp(s - np.where(live, row_lse + 0.5, 0.0)[:, None]), 0.0)"),
 }
