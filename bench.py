@@ -38,6 +38,10 @@ WORKLOADS = {
     "stripe": ("stripe", 262144, 8, [0], False),
     "contiguous": ("contiguous", 32768, 8, list(range(8)), False),
     "varlen": ("contiguous", 131072, 8, list(range(8)), True),
+    # per-sequence layouts: the same packed sequences, each laid out on its own
+    # (lengths rounded to multiples of 2N / N); rank 0 (zigzag: every rank equal)
+    "zigzag_varlen": ("zigzag_varlen", 131072, 8, [0], True),
+    "stripe_varlen": ("stripe_varlen", 131072, 8, [0], True),
 }
 HEADS, HEAD_DIM = 32, 128
 
@@ -73,9 +77,15 @@ def visible_pairs(qpos: np.ndarray, kpos: np.ndarray, cu) -> int:
     return int((hi - lo).sum())
 
 
+def _lcu(layout, cu):
+    """cu_seqlens as the layout functions take it (only the per-sequence layouts use it)."""
+    return cu if layout.endswith("_varlen") else None
+
+
 def step_pairs(ra, layout, S, N, r, cu):
-    qpos = ra.layout_positions(layout, S, N, r)
-    return [visible_pairs(qpos, ra.layout_positions(layout, S, N, (r - s) % N), cu) for s in range(N)]
+    qpos = ra.layout_positions(layout, S, N, r, _lcu(layout, cu))
+    return [visible_pairs(qpos, ra.layout_positions(layout, S, N, (r - s) % N, _lcu(layout, cu)), cu)
+            for s in range(N)]
 
 
 def cpu_baseline(layout, S, N, r, cu, D, seed=123):
@@ -88,7 +98,7 @@ def cpu_baseline(layout, S, N, r, cu, D, seed=123):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    qpos = oracle.layout_positions(layout, S, N, r)
+    qpos = oracle.layout_positions(layout, S, N, r, _lcu(layout, cu))
     rows = qpos[::8]
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((1, len(rows), 1, D))
@@ -147,12 +157,17 @@ def main():
     layout, S, N, ranks, varlen = WORKLOADS[args.workload]
     H, D = HEADS, HEAD_DIM
     L = S // N
-    cu = synth.cu_seqlens(synth.loguniform_lengths(S, 1024, 32768, seed=0)) if varlen else None
+    cu = None
+    if varlen:
+        lengths = synth.loguniform_lengths(S, 1024, 32768, seed=0)
+        if layout.endswith("_varlen"):
+            lengths = synth.round_lengths(lengths, 2 * N if layout == "zigzag_varlen" else N)
+        cu = synth.cu_seqlens(lengths)
 
     # Inputs: global Q, K, V, dO drawn on the GPU, laid out into the ring by the
     # library's positions; all resident before timing.
     q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=0, device=dev, with_dout=True)
-    idx = [torch.from_numpy(ra.layout_positions(layout, S, N, r)).to(dev) for r in range(N)]
+    idx = [torch.from_numpy(ra.layout_positions(layout, S, N, r, _lcu(layout, cu))).to(dev) for r in range(N)]
     k_ring = torch.stack([k.index_select(1, i) for i in idx]).contiguous()
     v_ring = torch.stack([v.index_select(1, i) for i in idx]).contiguous()
     del k, v
@@ -164,7 +179,8 @@ def main():
     dq = torch.empty((1, L, H, D), device=dev, dtype=torch.float32)
     dk_ring = torch.zeros(k_ring.shape, device=dev, dtype=torch.float32)
     dv_ring = torch.zeros(v_ring.shape, device=dev, dtype=torch.float32)
-    ws = torch.empty(ra.ring_workspace_bytes(layout, N, q_loc[ranks[0]]), device=dev, dtype=torch.uint8)
+    ws = torch.empty(ra.ring_workspace_bytes(layout, N, q_loc[ranks[0]], cu_seqlens=cu), device=dev,
+                     dtype=torch.uint8)
 
     pairs = {r: step_pairs(ra, layout, S, N, r, cu) for r in ranks}
     total_pairs = sum(sum(p) for p in pairs.values())
@@ -256,6 +272,7 @@ def main():
         "config": {
             "workload": (f"{layout} causal ring share{'s' if len(ranks) > 1 else ''} "
                          f"{'(varlen, log-uniform lengths in [1024, 32768]) ' if varlen else ''}"
+                         f"{'(lengths rounded to whole layout chunks) ' if layout.endswith('_varlen') else ''}"
                          f"fwd+bwd: seq {S}, ring of {N}, rank{'s' if len(ranks) > 1 else ''} "
                          f"{ranks if len(ranks) > 1 else ranks[0]}, {H} heads, head_dim {D}, batch 1"),
             "layout": layout, "seq_len": S, "world": N, "ranks": ranks, "heads": H, "head_dim": D,

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libra.so")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE = range(5)
-LAYOUT_IDS = {"contiguous": 0, "zigzag": 1, "stripe": 2}
+LAYOUT_IDS = {"contiguous": 0, "zigzag": 1, "stripe": 2, "zigzag_varlen": 3, "stripe_varlen": 4}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 
@@ -54,6 +54,7 @@ _SIGS = {
                     C.c_void_p, C.c_size_t, C.c_void_p],
     "ra_layout_positions": [C.c_int32, C.c_int64, C.c_int32, C.c_int32, P(C.c_int64)],
     "ra_layout_posmap": [C.c_int32, C.c_int64, C.c_int32, C.c_int32, P(ra_posmap)],
+    "ra_layout_positions_cu": [C.c_int32, P(C.c_int32), C.c_int32, C.c_int32, C.c_int32, P(C.c_int64)],
     "ra_cast_f32_to_bf16": [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p],
     "ra_timing_begin": [C.c_int32],
     "ra_timing_end": [P(ra_launch_time), C.c_int32, P(C.c_int32)],

@@ -75,8 +75,9 @@ class _Cu:
         if cu_seqlens is None:
             return
         if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+            # the host copy lets the library skip steps and split per-sequence layouts
             self.dev = cu_seqlens.to(torch.int32).contiguous()
-            self.host = None
+            self.host = np.ascontiguousarray(self.dev.cpu().numpy())
         else:
             self.host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
             self.dev = torch.from_numpy(self.host).to(device)
@@ -108,11 +109,20 @@ def _problem(x, heads: int, head_dim: int, seq_len: int, causal: bool, scale: Op
 
 # ---- layouts -------------------------------------------------------------------------------
 
-def layout_positions(layout: str, seq_len: int, world: int, rank: int) -> np.ndarray:
-    """Global positions of ``rank``'s local tokens (as the library lays them out)."""
+def layout_positions(layout: str, seq_len: int, world: int, rank: int, cu_seqlens=None) -> np.ndarray:
+    """Global positions of ``rank``'s local tokens (as the library lays them out).
+    The per-sequence layouts (``zigzag_varlen``, ``stripe_varlen``) need ``cu_seqlens``."""
     out = np.empty(seq_len // max(world, 1), dtype=np.int64)
-    check(lib().ra_layout_positions(_layout_id(layout), seq_len, world, rank,
-                                    out.ctypes.data_as(C.POINTER(C.c_int64))))
+    if cu_seqlens is None:
+        check(lib().ra_layout_positions(_layout_id(layout), seq_len, world, rank,
+                                        out.ctypes.data_as(C.POINTER(C.c_int64))))
+        return out
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+                                         dtype=np.int32))
+    if int(cu[-1]) != seq_len:
+        raise ValueError("cu_seqlens must end at seq_len")
+    check(lib().ra_layout_positions_cu(_layout_id(layout), cu.ctypes.data_as(C.POINTER(C.c_int32)), len(cu) - 1,
+                                       world, rank, out.ctypes.data_as(C.POINTER(C.c_int64))))
     return out
 
 
@@ -209,11 +219,12 @@ def ring_fwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, *, cau
     return out, lse, out_lowp
 
 
-def ring_workspace_bytes(layout: str, world: int, q_local, causal: bool = True, minimal: bool = False) -> int:
+def ring_workspace_bytes(layout: str, world: int, q_local, causal: bool = True, minimal: bool = False,
+                         cu_seqlens=None) -> int:
     """Workspace bytes ring_bwd uses: its fastest path (stored dS for bf16), or with
     ``minimal`` the least it accepts (dQ then recomputes S and dP)."""
     b, L, h, d = q_local.shape
-    p = _problem(q_local, h, d, L * world, causal, None, _Cu(None, None))
+    p = _problem(q_local, h, d, L * world, causal, None, _Cu(cu_seqlens, q_local.device))
     fn = lib().ra_ring_workspace_min_bytes if minimal else lib().ra_ring_workspace_bytes
     return int(fn(C.byref(p), _layout_id(layout), world))
 

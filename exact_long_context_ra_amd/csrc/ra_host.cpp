@@ -217,6 +217,10 @@ ra_status make_posmap(ra_layout layout, int64_t S, int32_t N, int32_t r, ra_posm
       m.seg[0] = ra_seg{r, N, S / N};
       break;
     }
+    case RA_LAYOUT_ZIGZAG_VARLEN:
+    case RA_LAYOUT_STRIPE_VARLEN:
+      return fail(RA_ERR_UNSUPPORTED, "layout %d has one posmap per sequence (see ra_layout_positions_cu)",
+                  (int)layout);
     default:
       return fail(RA_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
   }
@@ -329,6 +333,34 @@ ra_status ra_layout_positions(ra_layout layout, int64_t seq_len, int32_t world, 
   return RA_OK;
 }
 
+ra_status ra_layout_positions_cu(ra_layout layout, const int32_t* cu_host, int32_t num_seqs, int32_t world,
+                                 int32_t rank, int64_t* host_pos_out) {
+  RA_CHECK(host_pos_out != nullptr, RA_ERR_INVALID_ARG, "host_pos_out is NULL");
+  RA_CHECK(cu_host != nullptr && num_seqs >= 1, RA_ERR_INVALID_ARG, "cu_host with num_seqs >= 1 required");
+  RA_CHECK(cu_host[0] == 0, RA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < num_seqs; ++i)
+    RA_CHECK(cu_host[i + 1] >= cu_host[i], RA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing");
+  if (layout != RA_LAYOUT_ZIGZAG_VARLEN && layout != RA_LAYOUT_STRIPE_VARLEN)
+    return ra_layout_positions(layout, cu_host[num_seqs], world, rank, host_pos_out);
+  RA_CHECK(world >= 1 && rank >= 0 && rank < world, RA_ERR_INVALID_ARG, "rank %d / world %d out of range", rank,
+           world);
+  const ra_layout base = layout == RA_LAYOUT_ZIGZAG_VARLEN ? RA_LAYOUT_ZIGZAG : RA_LAYOUT_STRIPE;
+  int64_t a = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    ra_posmap m;
+    ra_status st = make_posmap(base, (int64_t)cu_host[i + 1] - cu_host[i], world, rank, &m);
+    if (st != RA_OK) {
+      char why[sizeof(g_err)];
+      snprintf(why, sizeof(why), "%s", g_err);
+      return fail(st, "sequence %d: %s", i, why);
+    }
+    for (int k = 0; k < m.nseg; ++k)
+      for (int64_t j = 0; j < m.seg[k].len; ++j)
+        host_pos_out[a++] = cu_host[i] + m.seg[k].begin + j * m.seg[k].stride;
+  }
+  return RA_OK;
+}
+
 ra_status ra_timing_begin(int32_t capacity) {
   RA_CHECK(capacity >= 1 && capacity <= RA_MAX_TIMED_LAUNCHES, RA_ERR_INVALID_ARG, "capacity %d out of range",
            capacity);
@@ -399,6 +431,7 @@ ra_status ra_block_attn_fwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_
   a.batch = prob->batch;
   a.heads = prob->heads;
   a.lq = (int32_t)lq;
+  a.lse_sh = lq;
   a.lk = (int32_t)lk;
   a.qmap = to_dmap(qmap);
   if (lk > 0) a.kmap = to_dmap(kmap);
@@ -490,6 +523,7 @@ static ra_status bwd_args(const ra_problem* prob, ra_tensor q, int64_t lq, const
   a.batch = prob->batch;
   a.heads = prob->heads;
   a.lq = (int32_t)lq;
+  a.lse_sh = lq;
   a.lk = (int32_t)lk;
   a.qmap = to_dmap(qmap);
   a.kmap = to_dmap(kmap);
@@ -530,50 +564,99 @@ ra_status ra_block_attn_bwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_
 
 // ---- virtual ring -------------------------------------------------------------------------
 
-static ra_status ring_common(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, int64_t* L) {
+static bool per_seq_layout(ra_layout l) { return l == RA_LAYOUT_ZIGZAG_VARLEN || l == RA_LAYOUT_STRIPE_VARLEN; }
+static ra_layout base_layout(ra_layout l) {
+  return l == RA_LAYOUT_ZIGZAG_VARLEN ? RA_LAYOUT_ZIGZAG : l == RA_LAYOUT_STRIPE_VARLEN ? RA_LAYOUT_STRIPE : l;
+}
+
+// One independent ring: the whole problem for the plain layouts; one packed
+// sequence for the per-sequence layouts (sequences never attend to each other,
+// and each one's local tokens are the run of rows [row0, row0 + L) of every
+// rank's buffers).  `prob` is the piece's own problem: for a sequence, its
+// length as seq_len and no cu_seqlens (one sequence, positions from 0).
+struct Piece {
+  ra_problem prob;
+  int64_t row0, L;
+};
+
+static ra_status ring_pieces(const ra_problem* prob, ra_layout layout, int32_t world, std::vector<Piece>* out) {
+  out->clear();
+  if (!per_seq_layout(layout)) {
+    ra_posmap m;
+    ra_status st = make_posmap(layout, prob->seq_len, world, 0, &m);
+    if (st != RA_OK) return st;
+    out->push_back(Piece{*prob, 0, prob->seq_len / world});
+    return RA_OK;
+  }
+  RA_CHECK(prob->num_seqs > 0 && prob->cu_seqlens != nullptr && prob->cu_seqlens_host != nullptr,
+           RA_ERR_INVALID_ARG, "layout %d needs cu_seqlens and its host copy", (int)layout);
+  const int64_t unit = layout == RA_LAYOUT_ZIGZAG_VARLEN ? 2 * (int64_t)world : world;
+  const int32_t* cu = prob->cu_seqlens_host;
+  for (int i = 0; i < prob->num_seqs; ++i) {
+    const int64_t n = (int64_t)cu[i + 1] - cu[i];
+    RA_CHECK(n % unit == 0, RA_ERR_INVALID_ARG, "sequence %d: length %lld not divisible by %lld", i, (long long)n,
+             (long long)unit);
+    if (n == 0) continue;
+    Piece pc{*prob, cu[i] / world, n / world};
+    pc.prob.seq_len = n;
+    pc.prob.cu_seqlens = nullptr;
+    pc.prob.cu_seqlens_host = nullptr;
+    pc.prob.num_seqs = 0;
+    out->push_back(pc);
+  }
+  return RA_OK;
+}
+
+static ra_status ring_common(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, int64_t* L,
+                             std::vector<Piece>* pieces) {
   ra_status st = check_problem(prob);
   if (st != RA_OK) return st;
   RA_CHECK(world >= 1, RA_ERR_INVALID_ARG, "world must be >= 1");
   RA_CHECK(rank >= 0 && rank < world, RA_ERR_INVALID_ARG, "rank %d out of range [0, %d)", rank, world);
-  ra_posmap m;
-  st = make_posmap(layout, prob->seq_len, world, rank, &m);
-  if (st != RA_OK) return st;
+  RA_CHECK(layout >= RA_LAYOUT_CONTIGUOUS && layout <= RA_LAYOUT_STRIPE_VARLEN, RA_ERR_INVALID_ARG,
+           "unknown layout %d", (int)layout);
+  if ((st = ring_pieces(prob, layout, world, pieces)) != RA_OK) return st;
   *L = prob->seq_len / world;
   return RA_OK;
 }
 
-ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
-                      ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, float* lse,
-                      ra_tensor out_lowp, void* stream) {
-  int64_t L = 0;
-  ra_status st = ring_common(prob, layout, world, rank, &L);
-  if (st != RA_OK) return st;
-  if (L == 0) return RA_OK;
+// rows further down a [b, rows, h, d] tensor
+static ra_tensor shift_rows(const ra_tensor& t, int64_t rows, size_t esz) {
+  ra_tensor u = t;
+  if (t.ptr) u.ptr = (char*)t.ptr + rows * t.stride_t * (int64_t)esz;
+  return u;
+}
+
+// The forward ring of one piece: rows [row0, row0 + pc.L) of the local buffers;
+// lse rows at lse + row0 with head stride lse_sh.
+static ra_status ring_fwd_piece(const Piece& pc, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                                ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, float* lse,
+                                int64_t lse_sh, ra_tensor out_lowp, hipStream_t s) {
+  const ra_problem* prob = &pc.prob;
+  const int64_t L = pc.L;
   const size_t esz = elem_size(prob->dtype);
-  if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("k_ring", k_ring, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("v_ring", v_ring, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("out_lowp", out_lowp, esz, L, out_lowp.ptr != nullptr)) != RA_OK) return st;
-  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
-  RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
-           "stride_rank must be >= 0 and keep 16-byte alignment");
+  q_local = shift_rows(q_local, pc.row0, esz);
+  k_ring = shift_rows(k_ring, pc.row0, esz);
+  v_ring = shift_rows(v_ring, pc.row0, esz);
+  out = shift_rows(out, pc.row0, 4);
+  out_lowp = shift_rows(out_lowp, pc.row0, esz);
 
   ra_posmap qmap;
   make_posmap(layout, prob->seq_len, world, rank, &qmap);
   std::vector<int> steps;
   std::vector<ra_posmap> kmaps(world);
-  for (int s = 0; s < world; ++s) {
-    const int src = ((rank - s) % world + world) % world;
-    make_posmap(layout, prob->seq_len, world, src, &kmaps[s]);
-    if (step_has_pairs(prob, qmap, L, kmaps[s], L)) steps.push_back(s);
+  for (int st = 0; st < world; ++st) {
+    const int src = ((rank - st) % world + world) % world;
+    make_posmap(layout, prob->seq_len, world, src, &kmaps[st]);
+    if (step_has_pairs(prob, qmap, L, kmaps[st], L)) steps.push_back(st);
   }
   if (steps.empty()) steps.push_back(0);  // still writes (0, -inf) rows
 
   FwdArgs a{};
   a.q = rd(q_local);
   a.out = wr(out);
-  a.lse = lse;
+  a.lse = lse + pc.row0;
+  a.lse_sh = lse_sh;
   a.batch = prob->batch;
   a.heads = prob->heads;
   a.lq = (int32_t)L;
@@ -583,7 +666,6 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   a.scale_log2 = scale_of(prob) * 1.4426950408889634f;
   a.n_qtiles = ceil_div(L, FWD_BQ);
   const bool bf16 = prob->dtype == RA_DTYPE_BF16;
-  hipStream_t s = (hipStream_t)stream;
   for (size_t i = 0; i < steps.size(); ++i) {
     const int step = steps[i];
     const int src = ((rank - step) % world + world) % world;
@@ -597,34 +679,74 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   return RA_OK;
 }
 
-// Workspace of ra_ring_bwd: delta [b, h, L] fp32 (rounded up to 256 bytes), then
-// for bf16 the dS^T buffer: per (b, h) a blocked [keys][query rows] slice of
-// round_up(L, 128) keys (whole dK/dV key tiles) by ds_ld = round_up(L, 128) rows
-// (whole dQ row tiles), bf16.
-static int64_t ds_ld_of(int64_t L) { return (L + FWD_BQ - 1) / FWD_BQ * FWD_BQ; }
-
-size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
-  if (check_problem(prob) != RA_OK || world < 1) return 0;
-  ra_posmap m;
-  if (make_posmap(layout, prob->seq_len, world, 0, &m) != RA_OK) return 0;
-  const int64_t L = prob->seq_len / world;
-  const size_t bytes = (size_t)prob->batch * prob->heads * L * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                      ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, float* lse,
+                      ra_tensor out_lowp, void* stream) {
+  int64_t L = 0;
+  std::vector<Piece> pieces;
+  ra_status st = ring_common(prob, layout, world, rank, &L, &pieces);
+  if (st != RA_OK) return st;
+  if (L == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("k_ring", k_ring, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("v_ring", v_ring, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("out_lowp", out_lowp, esz, L, out_lowp.ptr != nullptr)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
+           "stride_rank must be >= 0 and keep 16-byte alignment");
+  hipStream_t s = (hipStream_t)stream;
+  for (const Piece& pc : pieces) {
+    st = ring_fwd_piece(pc, base_layout(layout), world, rank, q_local, k_ring, v_ring, stride_rank, out, lse, L,
+                        out_lowp, s);
+    if (st != RA_OK) return st;
+  }
+  return RA_OK;
 }
 
-// dS^T bytes for the stored-dS path, or 0 where that path does not apply (fp32,
-// or one (b, h) slice too large for the kernels' 32-bit buffer offsets).
-static size_t ds_bytes(const ra_problem* prob, int64_t L) {
-  if (prob->dtype != RA_DTYPE_BF16 || L == 0) return 0;
-  const int64_t slice = (L + BWD_BK - 1) / BWD_BK * BWD_BK * ds_ld_of(L) * 2;
+// Workspace of ra_ring_bwd: delta [b, h, L] fp32 (rounded up to 256 bytes), then
+// for bf16 the dS^T buffer of one piece at a time: per (b, h) a blocked
+// [keys][query rows] slice of round_up(Lp, 128) keys (whole dK/dV key tiles) by
+// ds_ld = round_up(Lp, 128) rows (whole dQ row tiles), bf16, for the largest
+// piece length Lp.
+static int64_t ds_ld_of(int64_t L) { return (L + FWD_BQ - 1) / FWD_BQ * FWD_BQ; }
+
+// dS^T bytes of a piece of Lp local rows, or 0 where the stored-dS path does
+// not apply (fp32, or one (b, h) slice too large for 32-bit buffer offsets).
+static size_t ds_bytes(const ra_problem* prob, int64_t Lp) {
+  if (prob->dtype != RA_DTYPE_BF16 || Lp == 0) return 0;
+  const int64_t slice = (Lp + BWD_BK - 1) / BWD_BK * BWD_BK * ds_ld_of(Lp) * 2;
   if (slice >= ((int64_t)1 << 31)) return 0;
   return (size_t)prob->batch * prob->heads * (size_t)slice;
+}
+
+// Every piece must fit the stored-dS path for it to be used (0 otherwise).
+static size_t ds_bytes_max(const std::vector<Piece>& pieces) {
+  size_t m = 0;
+  for (const Piece& pc : pieces) {
+    const size_t b = ds_bytes(&pc.prob, pc.L);
+    if (b == 0) return 0;
+    m = b > m ? b : m;
+  }
+  return m;
+}
+
+size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
+  int64_t L = 0;
+  std::vector<Piece> pieces;
+  if (ring_common(prob, layout, world, 0, &L, &pieces) != RA_OK) return 0;
+  const size_t bytes = (size_t)prob->batch * prob->heads * L * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
 }
 
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
   const size_t base = ra_ring_workspace_min_bytes(prob, layout, world);
   if (base == 0) return 0;
-  return base + ds_bytes(prob, prob->seq_len / world);
+  int64_t L = 0;
+  std::vector<Piece> pieces;
+  ring_common(prob, layout, world, 0, &L, &pieces);
+  return base + ds_bytes_max(pieces);
 }
 
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
@@ -632,7 +754,8 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
                       ra_tensor dout, ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
                       void* workspace, size_t workspace_bytes, void* stream) {
   int64_t L = 0;
-  ra_status st = ring_common(prob, layout, world, rank, &L);
+  std::vector<Piece> pieces;
+  ra_status st = ring_common(prob, layout, world, rank, &L, &pieces);
   if (st != RA_OK) return st;
   if (L == 0) return RA_OK;
   const size_t esz = elem_size(prob->dtype);
@@ -653,11 +776,9 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
            "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-  const size_t dsb = ds_bytes(prob, L);
+  const size_t dsb = ds_bytes_max(pieces);
   uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
 
-  ra_posmap qmap;
-  make_posmap(layout, prob->seq_len, world, rank, &qmap);
   float* delta = (float*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = prob->dtype == RA_DTYPE_BF16;
@@ -675,19 +796,30 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   RA_HIP(timed(K_ZERO, -1, s, [&] {
     return launch_zero(dqw, prob->batch, prob->heads, (int32_t)L, prob->head_dim, s);
   }));
-  for (int step = 0; step < world; ++step) {
-    const int src = ((rank - step) % world + world) % world;
-    ra_posmap kmap;
-    make_posmap(layout, prob->seq_len, world, src, &kmap);
-    if (!step_has_pairs(prob, qmap, L, kmap, L)) continue;
-    BwdArgs a;
-    bwd_args(prob, q_local, L, qmap, offset_rd(k_ring, src * stride_rank, esz),
-             offset_rd(v_ring, src * stride_rank, esz), L, kmap, dout, lse, delta, dqw,
-             offset_wr(dk_ring, src * stride_rank_grad, 4), offset_wr(dv_ring, src * stride_rank_grad, 4), &a);
-    a.dsT = dsT;
-    a.ds_ld = ds_ld_of(L);
-    ra_status st2 = launch_bwd_step(a, prob->head_dim, bf16, step, s);
-    if (st2 != RA_OK) return st2;
+  const ra_layout lay = base_layout(layout);
+  for (const Piece& pc : pieces) {
+    const ra_problem* pp = &pc.prob;
+    const ra_tensor qp = shift_rows(q_local, pc.row0, esz), kp = shift_rows(k_ring, pc.row0, esz);
+    const ra_tensor vp = shift_rows(v_ring, pc.row0, esz), dop = shift_rows(dout, pc.row0, esz);
+    const ra_tensor dqp = shift_rows(dq, pc.row0, 4), dkp = shift_rows(dk_ring, pc.row0, 4);
+    const ra_tensor dvp = shift_rows(dv_ring, pc.row0, 4);
+    ra_posmap qmap;
+    make_posmap(lay, pp->seq_len, world, rank, &qmap);
+    for (int step = 0; step < world; ++step) {
+      const int src = ((rank - step) % world + world) % world;
+      ra_posmap kmap;
+      make_posmap(lay, pp->seq_len, world, src, &kmap);
+      if (!step_has_pairs(pp, qmap, pc.L, kmap, pc.L)) continue;
+      BwdArgs a;
+      bwd_args(pp, qp, pc.L, qmap, offset_rd(kp, src * stride_rank, esz), offset_rd(vp, src * stride_rank, esz),
+               pc.L, kmap, dop, lse + pc.row0, delta + pc.row0, wr(dqp), offset_wr(dkp, src * stride_rank_grad, 4),
+               offset_wr(dvp, src * stride_rank_grad, 4), &a);
+      a.lse_sh = L;
+      a.dsT = dsT;
+      a.ds_ld = ds_ld_of(pc.L);
+      ra_status st2 = launch_bwd_step(a, pp->head_dim, bf16, step, s);
+      if (st2 != RA_OK) return st2;
+    }
   }
   return RA_OK;
 }

@@ -38,7 +38,8 @@ enum FwdMode : int32_t { FWD_STORE = 0, FWD_MERGE = 1 };
 struct FwdArgs {
   Tensor4 q, k, v;
   Tensor4W out;      // fp32
-  float* lse;        // fp32 [b, h, lq]
+  float* lse;        // fp32, row t of (batch b, head h) at lse[(b*heads + h)*lse_sh + t]
+  int64_t lse_sh;    // head stride of lse (lq unless the rows are a slice of a longer buffer)
   Tensor4W out_lowp; // optional, ptr may be null; same dtype as q
   int32_t batch, heads, lq, lk;
   DMap qmap, kmap;
@@ -50,8 +51,9 @@ struct FwdArgs {
 
 struct BwdArgs {
   Tensor4 q, k, v, dout;
-  const float* lse;    // [b, h, lq] natural log (final)
-  const float* delta;  // [b, h, lq]
+  const float* lse;    // natural log (final); row t of (b, h) at lse[(b*heads + h)*lse_sh + t]
+  const float* delta;  // same indexing as lse
+  int64_t lse_sh;      // head stride of lse and delta (lq unless the rows are a slice)
   Tensor4W dq, dk, dv; // fp32 accumulators
   int32_t batch, heads, lq, lk;
   DMap qmap, kmap;

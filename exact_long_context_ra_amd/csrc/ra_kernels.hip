@@ -469,7 +469,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     lse_b = NEG_INF;
     inv = 0.f;
   }
-  float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lq + row;
+  float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lse_sh + row;
   float* orow = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)row * a.out.st + head * a.out.sh;
   float wa = 0.f, wb = inv, lse_new = lse_b;
   if (a.mode == FWD_MERGE) {
@@ -675,8 +675,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_kernel(BwdArgs a) {
   const Rsrc rdo = make_rsrc(dobase, slice_bytes(a.lq, a.dout.st, ESZ, D));
   const uint32_t qst = (uint32_t)(a.q.st * ESZ), kst = (uint32_t)(a.k.st * ESZ);
   const uint32_t vst = (uint32_t)(a.v.st * ESZ), dst = (uint32_t)(a.dout.st * ESZ);
-  const float* lse_b = a.lse + ((int64_t)b * a.heads + head) * a.lq;
-  const float* del_b = a.delta + ((int64_t)b * a.heads + head) * a.lq;
+  const float* lse_b = a.lse + ((int64_t)b * a.heads + head) * a.lse_sh;
+  const float* del_b = a.delta + ((int64_t)b * a.heads + head) * a.lse_sh;
   float* dqb = reinterpret_cast<float*>(a.dq.ptr) + b * a.dq.sb + head * a.dq.sh;
 
   const int k_first = kt * BWD_BK;
@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
     lse_b = NEG_INF;
     inv = 0.f;
   }
-  float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lq + row;
+  float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lse_sh + row;
   float* orow = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)row * a.out.st + head * a.out.sh;
   float wa = 0.f, wb = inv, lse_new = lse_b;
   if (a.mode == FWD_MERGE) {
@@ -1292,8 +1292,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
   const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, 2, D));
   const Rsrc rdo = make_rsrc(dobase, slice_bytes(a.lq, a.dout.st, 2, D));
-  const Rsrc rlse = make_rsrc(a.lse + ((int64_t)b * a.heads + head) * a.lq, (uint32_t)a.lq * 4);
-  const Rsrc rdel = make_rsrc(a.delta + ((int64_t)b * a.heads + head) * a.lq, (uint32_t)a.lq * 4);
+  const Rsrc rlse = make_rsrc(a.lse + ((int64_t)b * a.heads + head) * a.lse_sh, (uint32_t)a.lq * 4);
+  const Rsrc rdel = make_rsrc(a.delta + ((int64_t)b * a.heads + head) * a.lse_sh, (uint32_t)a.lq * 4);
   const uint32_t qst = (uint32_t)(a.q.st * 2), kst = (uint32_t)(a.k.st * 2);
   const uint32_t vst = (uint32_t)(a.v.st * 2), dst = (uint32_t)(a.dout.st * 2);
 
@@ -1585,9 +1585,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   float lse2 = POS_INF, dl = 0.f;
   if (row_ok) {
-    const float x = a.lse[((int64_t)b * a.heads + head) * a.lq + row];
+    const float x = a.lse[((int64_t)b * a.heads + head) * a.lse_sh + row];
     lse2 = (x == NEG_INF) ? POS_INF : x * LOG2E;
-    dl = a.delta[((int64_t)b * a.heads + head) * a.lq + row];
+    dl = a.delta[((int64_t)b * a.heads + head) * a.lse_sh + row];
   }
 
   const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, min(row, r_last)));

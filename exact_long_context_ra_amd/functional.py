@@ -30,9 +30,10 @@ def _torch():
     return torch
 
 
-def _positions(layout: str, S: int, world: int, device):
+def _positions(layout: str, S: int, world: int, device, cu_seqlens=None):
     torch = _torch()
-    return [torch.from_numpy(api.layout_positions(layout, S, world, r)).to(device) for r in range(world)]
+    cu = cu_seqlens if layout.endswith("_varlen") else None  # only the per-sequence layouts use it
+    return [torch.from_numpy(api.layout_positions(layout, S, world, r, cu)).to(device) for r in range(world)]
 
 
 class _VirtualRing:
@@ -42,7 +43,7 @@ class _VirtualRing:
     def forward(q, k, v, layout, world, causal, cu_seqlens, scale):
         torch = _torch()
         b, S, h, d = q.shape
-        idx = _positions(layout, S, world, q.device)
+        idx = _positions(layout, S, world, q.device, cu_seqlens)
         k_ring = torch.stack([k.index_select(1, i) for i in idx]).contiguous()
         v_ring = torch.stack([v.index_select(1, i) for i in idx]).contiguous()
         out = torch.empty((b, S, h, d), device=q.device, dtype=q.dtype)
@@ -128,7 +129,9 @@ def ring_attn_varlen_func(q, k, v, cu_seqlens: Sequence[int], *, layout: str = "
                           causal: bool = True, softmax_scale: Optional[float] = None, return_lse: bool = False):
     """Packed variable-length form: q/k/v are [1, T, h, d] (or [T, h, d]) holding
     several sequences back to back, delimited by ONE cu_seqlens shared by q and
-    k/v (int32 global offsets, first 0, last T)."""
+    k/v (int32 global offsets, first 0, last T).  ``layout`` lays out the packed
+    stream as a whole (contiguous, zigzag, stripe) or every sequence on its own
+    (zigzag_varlen, stripe_varlen: each length divisible by 2*world / world)."""
     global _FN
     if _FN is None:
         _FN = _make_function()

@@ -65,7 +65,18 @@ typedef enum {
  *  STRIPE:     token t lives on rank t mod N ("Striped Ring Attention" section
  *              of the guijiagi.com Ring Attention article; Striped Attention
  *              abstract on briefgpt.xyz). */
-typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_ZIGZAG = 1, RA_LAYOUT_STRIPE = 2 } ra_layout;
+/* Token-to-rank layouts.  The *_VARLEN layouts apply zigzag / stripe to every
+ * packed sequence of cu_seqlens on its own (the README lists zigzag and stripe
+ * forms of the varlen ring function): rank r holds its part of sequence 0,
+ * then of sequence 1, and so on.  They need cu_seqlens (with its host copy),
+ * and every sequence length divisible by 2*world (zigzag) or world (stripe). */
+typedef enum {
+  RA_LAYOUT_CONTIGUOUS = 0,
+  RA_LAYOUT_ZIGZAG = 1,
+  RA_LAYOUT_STRIPE = 2,
+  RA_LAYOUT_ZIGZAG_VARLEN = 3,
+  RA_LAYOUT_STRIPE_VARLEN = 4
+} ra_layout;
 
 typedef enum { RA_DTYPE_F32 = 0, RA_DTYPE_BF16 = 1 } ra_dtype;
 
@@ -148,7 +159,9 @@ ra_status ra_block_attn_bwd(const ra_problem* prob,
  *  out_lowp: optional copy of the final output in prob->dtype (ptr NULL = none).
  * Each step's block result is folded into out/lse by the lse merge inside the
  * attention kernel's epilogue (fp32 throughout); steps without any visible pair
- * are not launched. */
+ * are not launched.  With a *_VARLEN layout (cu_seqlens and its host copy
+ * required) the sequences never attend to each other, so each sequence's rows
+ * (a contiguous run of the local tokens) run as a ring of their own. */
 ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
                       ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
                       ra_tensor out, float* lse, ra_tensor out_lowp, void* stream);
@@ -185,7 +198,14 @@ size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int
 ra_status ra_layout_positions(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank,
                               int64_t* host_pos_out);
 
-/* The posmap ra_ring_fwd/bwd use for `rank` (host struct). */
+/* As ra_layout_positions, for any layout including the *_VARLEN ones:
+ * cu_host[0..num_seqs] are the packed sequences' global offsets (host memory;
+ * ignored by the other layouts, seq_len = cu_host[num_seqs]). */
+ra_status ra_layout_positions_cu(ra_layout layout, const int32_t* cu_host, int32_t num_seqs, int32_t world,
+                                 int32_t rank, int64_t* host_pos_out);
+
+/* The posmap ra_ring_fwd/bwd use for `rank` (host struct; not for *_VARLEN layouts,
+ * whose posmaps have a pair of segments per sequence). */
 ra_status ra_layout_posmap(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank,
                            ra_posmap* out);
 

@@ -59,3 +59,17 @@ def loguniform_lengths(total: int, lo: int, hi: int, seed: int) -> List[int]:
 def cu_seqlens(lengths: Sequence[int]) -> np.ndarray:
     """int32 offsets [0, l0, l0+l1, ...] of packed sequences."""
     return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def round_lengths(lengths, unit: int):
+    """Round packed sequence lengths down to multiples of ``unit`` (at least one
+    unit each), giving what that removes to the last sequence, so the total is
+    unchanged (it must itself be a multiple of ``unit``)."""
+    total = int(sum(lengths))
+    if total % unit:
+        raise ValueError("total length must be a multiple of unit")
+    out = [max(unit, (int(n) // unit) * unit) for n in lengths]
+    out[-1] += total - sum(out)
+    if out[-1] <= 0:
+        raise ValueError("lengths too short to round")
+    return out

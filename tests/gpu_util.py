@@ -76,10 +76,23 @@ def check_grad(got, ref, dtype_is_bf16: bool, what="grad"):
     return err
 
 
-def ring_from_global(x, layout: str, world: int):
-    """[b, S, h, d] -> [world, b, S/world, h, d] using the library's positions."""
+def ring_from_global(x, layout: str, world: int, cu_seqlens=None):
+    """[b, S, h, d] -> [world, b, S/world, h, d] using the library's positions
+    (the per-sequence layouts need cu_seqlens)."""
     import torch
     import exact_long_context_ra_amd as ra
     S = x.shape[1]
-    idx = [torch.from_numpy(ra.layout_positions(layout, S, world, r)).to(x.device) for r in range(world)]
+    cu = cu_seqlens if layout.endswith("_varlen") else None
+    idx = [torch.from_numpy(ra.layout_positions(layout, S, world, r, cu)).to(x.device) for r in range(world)]
     return torch.stack([x.index_select(1, i) for i in idx]).contiguous(), idx
+
+
+def varlen_cu_multiple(S: int, unit: int):
+    """cu_seqlens of packed lengths that are multiples of `unit` (as the
+    per-sequence layouts need): single units, an empty sequence, runs that
+    straddle tiles, and the rest of S as the last sequence."""
+    import synth
+    lengths = [unit, 0, 8 * unit, unit, 17 * unit, 33 * unit, unit]
+    rest = S - sum(lengths)
+    assert rest > 0 and rest % unit == 0
+    return synth.cu_seqlens(lengths + [rest])

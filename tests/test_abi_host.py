@@ -80,6 +80,29 @@ def test_pair_counts_from_library_positions(ra, layout):
         assert got == closed_form_pairs(layout, S, N, r)
 
 
+@pytest.mark.parametrize("layout", ["zigzag_varlen", "stripe_varlen"])
+def test_per_sequence_positions_match_oracle(ra, layout):
+    for N, cu in [(1, [0, 6, 24]), (2, [0, 8, 24]), (4, [0, 8, 8, 64, 128]), (8, [0, 16, 16, 4096, 8192])]:
+        S = cu[-1]
+        for r in range(N):
+            got = ra.layout_positions(layout, S, N, r, cu)
+            assert np.array_equal(got, oracle.layout_positions(layout, S, N, r, cu)), (layout, N, cu, r)
+
+
+def test_per_sequence_validation(ra):
+    from exact_long_context_ra_amd._lib import RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED
+    lib = ra.lib()
+    assert _ring_fwd(ra, _problem(ra), layout=3) == RA_ERR_INVALID_ARG  # needs cu_seqlens
+    assert b"cu_seqlens" in lib.ra_last_error()
+    cu_bad = (C.c_int32 * 3)(0, 20, 64)  # 20 is not a multiple of 2*world = 8
+    p = _problem(ra, num_seqs=2, cu_seqlens=4096, cu_seqlens_host=C.cast(cu_bad, C.c_void_p))
+    assert _ring_fwd(ra, p, layout=3) == RA_ERR_INVALID_ARG
+    assert b"not divisible" in lib.ra_last_error()
+    with pytest.raises(ra.RAError):
+        ra.layout_posmap("zigzag_varlen", 64, 4, 0)
+    assert lib.ra_layout_posmap(3, 64, 4, 0, C.byref(ra.posmap([(0, 1, 16)]))) == RA_ERR_UNSUPPORTED
+
+
 def _problem(ra, **kw):
     from exact_long_context_ra_amd._lib import ra_problem
     p = ra_problem()

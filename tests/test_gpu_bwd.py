@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_grad, dev, f64, log, ring_from_global
+from gpu_util import varlen_cu_multiple, check_grad, dev, f64, log, ring_from_global
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,9 @@ RING_BWD_CASES = [
     ("zigzag", 800, 4, 2, 64, "bf16", None),
     ("contiguous", 1536, 4, 2, 128, "bf16", "varlen"),
     ("stripe", 1536, 4, 2, 128, "f32", "varlen"),
+    ("zigzag_varlen", 1536, 4, 2, 128, "bf16", "varlen"),
+    ("stripe_varlen", 1536, 4, 2, 64, "bf16", "varlen"),
+    ("zigzag_varlen", 1536, 4, 2, 64, "f32", "varlen"),
 ]
 
 
@@ -97,14 +100,16 @@ def test_ring_bwd(case, store_ds):
     ra = _ra()
     layout, S, N, H, D, dt, cu = case
     log(f"ring_bwd {case} store_ds={store_ds}")
-    if cu == "varlen":
+    if cu == "varlen" and layout.endswith("_varlen"):
+        cu = varlen_cu_multiple(S, 2 * N if layout == "zigzag_varlen" else N)
+    elif cu == "varlen":
         lengths = [1, 200, 1, 129, 300]
         lengths.append(S - sum(lengths))
         cu = synth.cu_seqlens(lengths)
     q, k, v, do = synth.qkv(S, H, D, _dtype(dt), seed=31, device="cpu", with_dout=True)
     q, k, v, do = (x.to(dev()) for x in (q, k, v, do))
-    kr, idx = ring_from_global(k, layout, N)
-    vr, _ = ring_from_global(v, layout, N)
+    kr, idx = ring_from_global(k, layout, N, cu)
+    vr, _ = ring_from_global(v, layout, N, cu)
     dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
     dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
     q64, k64, v64, do64 = f64(q), f64(k), f64(v), f64(do)
@@ -119,7 +124,7 @@ def test_ring_bwd(case, store_ds):
         dq, _, _ = ra.ring_bwd(layout, N, r, ql, kr, vr, out, lse, dol, causal=True, cu_seqlens=cu,
                                dk_ring=dk_ring, dv_ring=dv_ring, store_ds=store_ds)
         torch.cuda.synchronize()
-        opos = oracle.layout_positions(layout, S, N, r)
+        opos = oracle.layout_positions(layout, S, N, r, cu)
         check_grad(f64(dq), gq[:, opos], bf, what=f"dq r={r}")
-    check_grad(f64(dk_ring), oracle.to_ring(gk, layout, N), bf, what="dk (all ranks)")
-    check_grad(f64(dv_ring), oracle.to_ring(gv, layout, N), bf, what="dv (all ranks)")
+    check_grad(f64(dk_ring), oracle.to_ring(gk, layout, N, cu), bf, what="dk (all ranks)")
+    check_grad(f64(dv_ring), oracle.to_ring(gv, layout, N, cu), bf, what="dv (all ranks)")

@@ -69,18 +69,24 @@ def test_packed_forms_match_unpacked():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
-def test_varlen_func_autograd(dt):
+@pytest.mark.parametrize("dt,layout", [("bf16", "contiguous"), ("f32", "contiguous"),
+                                       ("bf16", "zigzag_varlen"), ("f32", "stripe_varlen")])
+def test_varlen_func_autograd(dt, layout):
     import torch
     ra = _ra()
-    log(f"varlen func {dt}")
-    lengths = [7, 1, 300, 129, 1, 586]
-    T, H, D, N = sum(lengths), 2, 128, 4
+    log(f"varlen func {dt} {layout}")
+    N = 4
+    if layout == "contiguous":
+        lengths = [7, 1, 300, 129, 1, 586]
+    else:  # per-sequence layouts: lengths divisible by 2N / N
+        u = 2 * N if layout == "zigzag_varlen" else N
+        lengths = [u, 38 * u, 16 * u, u, 72 * u]
+    T, H, D = sum(lengths), 2, 128
     cu = synth.cu_seqlens(lengths)
     q, k, v, do = synth.qkv(T, H, D, _dt(dt), seed=47, device="cpu", with_dout=True)
     q, k, v, do = (x[0].to(dev()) for x in (q, k, v, do))  # [T, h, d]
     qg, kg, vg = (x.clone().requires_grad_(True) for x in (q, k, v))
-    out = ra.ring_attn_varlen_func(qg, kg, vg, cu, layout="contiguous", world=N)
+    out = ra.ring_attn_varlen_func(qg, kg, vg, cu, layout=layout, world=N)
     out.backward(do)
     torch.cuda.synchronize()
     pos = np.arange(T)

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_lse, check_out, dev, f64, log, ring_from_global
+from gpu_util import check_lse, check_out, dev, f64, log, ring_from_global, varlen_cu_multiple
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +104,11 @@ RING_CASES = [
     ("contiguous", 1536, 4, 2, 128, "bf16", True, "varlen", 1),
     ("zigzag", 1536, 4, 2, 128, "f32", True, "varlen", 1),
     ("stripe", 1536, 4, 2, 64, "bf16", True, "varlen", 1),
+    # per-sequence layouts: every sequence zigzagged / striped on its own
+    ("zigzag_varlen", 1536, 4, 2, 128, "bf16", True, "varlen", 1),
+    ("zigzag_varlen", 1536, 4, 2, 64, "f32", True, "varlen", 1),
+    ("stripe_varlen", 1536, 4, 2, 128, "f32", True, "varlen", 1),
+    ("stripe_varlen", 2048, 8, 2, 64, "bf16", True, "varlen", 1),
 ]
 
 
@@ -120,12 +125,14 @@ def test_ring_fwd(case):
     ra = _ra()
     layout, S, N, H, D, dt, causal, cu, B = case
     log(f"ring_fwd {case}")
-    cu = _varlen_cu(S) if cu == "varlen" else None
+    if cu == "varlen":
+        per_seq = layout.endswith("_varlen")
+        cu = varlen_cu_multiple(S, 2 * N if layout == "zigzag_varlen" else N) if per_seq else _varlen_cu(S)
     seed = 0 if S == 512 else 11
     q, k, v = synth.qkv(S, H, D, _dtype(dt), seed=seed, device="cpu", batch=B)
     q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
-    kr, idx = ring_from_global(k, layout, N)
-    vr, _ = ring_from_global(v, layout, N)
+    kr, idx = ring_from_global(k, layout, N, cu)
+    vr, _ = ring_from_global(v, layout, N, cu)
     q64, k64, v64 = f64(q), f64(k), f64(v)
     allk = np.arange(S)
     bf = dt == "bf16"
@@ -133,7 +140,7 @@ def test_ring_fwd(case):
         ql = q.index_select(1, idx[r]).contiguous()
         out, lse, lowp = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=causal, cu_seqlens=cu, want_lowp=True)
         torch.cuda.synchronize()
-        opos = oracle.layout_positions(layout, S, N, r)
+        opos = oracle.layout_positions(layout, S, N, r, cu)
         assert np.array_equal(opos, idx[r].cpu().numpy())
         ro, rl = oracle.attention(q64[:, opos], k64, v64, opos, allk, causal, cu)
         check_out(f64(out), ro, bf, what=f"out r={r}")
