@@ -993,6 +993,12 @@ __device__ __forceinline__ void wait_vmem_keep() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+// Workgroup barrier without __syncthreads()' release fence, which waits for
+// every outstanding vector-memory operation of the wave, buffer->LDS copies
+// still in flight included.  The caller makes its own LDS writes complete with
+// explicit waits before it; the asm's memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_vmem() { asm volatile("s_barrier" ::: "memory"); }
 // Direct buffer->LDS copy of 64 consecutive fp32 values (one per lane).
 __device__ __forceinline__ void dma_f32x64(Rsrc rs, int first, char* dst, int lane) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (uint32_t)(first + lane) * 4, 0, 0, 0);
@@ -1675,35 +1681,45 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
-// dQ from the stored dS^T: a workgroup owns 128 query rows (32 per wave) and
-// walks the 64-key tiles they can see: dQ^T += K^T dS^T, both operands
-// through transposed reads of natural LDS tiles (the K tile, and the dS^T
-// tile [64 keys][128 rows]), DMA'd one tile ahead.  A wave skips a key tile
-// whose dK/dV workgroup did not visit the wave's query tile: nothing there is
-// visible and that block of dS^T was not written.
+// dQ from the stored dS^T: a workgroup of 8 waves owns 256 query rows (32 per
+// wave) and walks the 64-key tiles they can see: dQ^T += K^T dS^T, both
+// operands through transposed reads of natural LDS tiles (the K tile, shared
+// by all 8 waves, and two dS^T sub-tiles [64 keys][128 rows]).  The kernel
+// streams dS^T from HBM, so tiles are DMA'd two ahead through three LDS
+// buffers (three separate objects, each reached statically, so the compiler
+// waits only for the tile it reads).  A wave skips a key tile whose dK/dV
+// workgroup did not visit the wave's query tile: nothing there is visible and
+// that block of dS^T was not written.
+constexpr int DQS_ROWS = 256;  // query rows per dQ-from-dS workgroup
+
 template <int D>
 struct DqsB {
-  static constexpr int KT = DQ_BK * D * 2;       // K tile
-  static constexpr int ST = DQ_BK * FWD_BQ * 2;  // dS^T tile: 64 keys x 128 query rows
-  static constexpr int BUF = KT + ST;
-  static constexpr int LDS = 2 * BUF;
+  static constexpr int KT = DQ_BK * D * 2;  // K tile: 64 keys
+  static constexpr int ST = DQ_BK * 128 * 2;  // one dS^T sub-tile: 64 keys x 128 query rows
+  static constexpr int BUF = KT + 2 * ST;   // one stage
+  // buffer->LDS instructions each wave issues per stage (K tile, then the sub-tiles)
+  static constexpr int DMA_PER_STAGE = DQ_BK / 8 / (1024 / (2 * D)) + 2 * (DQ_BK / 8 / 4);
 };
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void bwd_dq_ds_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs a) {
   using C = DqsB<D>;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(16))) char sbuf0[C::BUF];
+  __shared__ __attribute__((aligned(16))) char sbuf1[C::BUF];
+  __shared__ __attribute__((aligned(16))) char sbuf2[C::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = w >> 2, wcol = w & 3;  // this wave's dS^T sub-tile and its 32-row column block
+  const int n_qt = (a.lq + DQS_ROWS - 1) / DQS_ROWS;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;
-  const int bh = logical / a.n_qtiles;
+  const int qt = n_qt - 1 - logical % n_qt;
+  const int bh = logical / n_qt;
   const int head = bh % a.heads, b = bh / a.heads;
 
-  const int r_first = qt * FWD_BQ;
-  const int r_last = min(a.lq, r_first + FWD_BQ) - 1;
+  const int r_first = qt * DQS_ROWS;
+  const int r_last = min(a.lq, r_first + DQS_ROWS) - 1;
   const int w_first = r_first + 32 * w;
   const bool wave_has_rows = w_first <= r_last;
   const int row = w_first + l32;
@@ -1716,21 +1732,6 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_ds_kernel(BwdArgs a) {
   // This (batch, head) slice of dS^T (blocked layout, see ds_offset).
   const int64_t ds_elems = ds_slice_elems(a.lk, a.ds_ld);
   const Rsrc rs = make_rsrc(a.dsT + (int64_t)(b * a.heads + head) * ds_elems, (uint32_t)(ds_elems * 2));
-  // DMA of the dS^T tile [64 keys][128 query rows] into a natural swizzled LDS
-  // tile: wave w moves tile rows (keys) 16*w .. 16*w+15, four per instruction;
-  // lane l fills LDS position l mod 16 of key 16*w + 4*i + l/16, which holds
-  // the chunk of 8 query rows c = position ^ swz(key).  Per instruction this
-  // gathers 8 runs of 128 contiguous bytes.
-  auto dma_ds = [&](int jt, char* tile) {
-#pragma unroll
-    for (int i = 0; i < DQ_BK / 16; ++i) {
-      const int kr = 16 * w + 4 * i + (lane >> 4);
-      const int c = (lane & 15) ^ swz<128>(kr);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(tile + (16 * w + 4 * i) * 256), 16,
-          (uint32_t)(ds_offset(jt * DQ_BK + kr, r_first + 8 * c, a.ds_ld) * 2), 0, 0, 0);
-    }
-  };
 
   const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
   const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
@@ -1741,22 +1742,58 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_ds_kernel(BwdArgs a) {
 #pragma unroll
   for (int d = 0; d < NDB; ++d) acc[d] = f32x16{};
 
+  // Per-lane byte offsets, within a stage, of the transposed reads of key rows
+  // 8*hf + (j >> 2) + 4*hi (j = lane mod 16) at column 32*d + 16*g1 + 4*(j & 3)
+  // (g1 = bit 4 of the lane) of the K tile, and at this wave's column block of
+  // its dS^T sub-tile.  Key rows 16*ks further sit at an immediate offset (the
+  // swizzle depends on the row modulo 16 only).  Keeping every address one
+  // register plus an immediate from the stage's buffer also lets the compiler
+  // tell the three buffers apart, so reading one does not wait for the DMA
+  // into another.
+  int offK[NDB][2], offS[2];
+  {
+    const int j = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hf + (j >> 2) + 4 * hi;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const int colb = 2 * (32 * d + 16 * g1 + 4 * (j & 3));
+        offK[d][hi] = nat_off<D>(r, colb >> 4) + (colb & 15);
+      }
+      const int colb = 2 * (32 * wcol + 16 * g1 + 4 * (j & 3));
+      offS[hi] = C::KT + half * C::ST + nat_off<128>(r, colb >> 4) + (colb & 15);
+    }
+  }
+
+  // One stage: the K tile (8 rows per wave), then dS^T keys 8w .. 8w+7 of both
+  // sub-tiles into natural swizzled [64][128] tiles: lane l fills LDS position
+  // l mod 16 of key 8w + 4i + l/16, which holds the chunk of 8 query rows
+  // c = position ^ swz(key).  Each instruction gathers 8 runs of 128 bytes.
+  auto issue = [&](int jt, char* buf) {
+    dma_tile<D, DQ_BK, 8>(rk, kst, jt * DQ_BK, buf, w, lane);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kr = 8 * w + 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ swz<128>(kr);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)(buf + C::KT + sub * C::ST + (8 * w + 4 * i) * 256), 16,
+            (uint32_t)(ds_offset(jt * DQ_BK + kr, r_first + 128 * sub + 8 * c, a.ds_ld) * 2), 0, 0, 0);
+      }
+  };
+
   if (kbeg < kend) {
     const int jt0 = kbeg / DQ_BK, jt1 = (kend - 1) / DQ_BK;
-    auto issue = [&](int jt, char* buf) {
-      dma_tile<D, DQ_BK>(rk, kst, jt * DQ_BK, buf, w, lane);
-      dma_ds(jt, buf + C::KT);
-    };
-    issue(jt0, smem);
-    wait_vmem();
-    __syncthreads();
     int cov_tile = -1;
     bool covered = false;
-    for (int jt = jt0; jt <= jt1; ++jt) {
-      const int cur = (jt - jt0) & 1;
-      const char* sK = smem + cur * C::BUF;
-      const char* sS = sK + C::KT;
-      if (jt < jt1) issue(jt + 1, smem + (cur ^ 1) * C::BUF);
+    // Tile jt from `cur` while tile jt + 2 is fetched into `nxt2` (which held
+    // tile jt - 1); at the end, wait until tile jt + 1 has landed, leaving tile
+    // jt + 2 in flight.  Past the last tile the last one is fetched again into
+    // the free buffer, so that every step issues the same copies.
+    auto step = [&](int jt, const char* cur, char* nxt2) {
+      issue(min(jt + 2, jt1), nxt2);
       const int kt = jt * DQ_BK / BWD_BK;
       if (kt != cov_tile) {
         int q0, q1;
@@ -1767,14 +1804,30 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_ds_kernel(BwdArgs a) {
       if (wave_has_rows && covered) {
 #pragma unroll
         for (int ks = 0; ks < DQ_BK / 16; ++ks) {
-          const bf16x8 sop = tr_operand<128>(sS, 16 * ks + 8 * hf, w, lane);
+          const u32x2 slo = tr16(cur + offS[0] + ks * 16 * 256), shi = tr16(cur + offS[1] + ks * 16 * 256);
+          const bf16x8 sop = __builtin_bit_cast(bf16x8, u32x4{slo[0], slo[1], shi[0], shi[1]});
 #pragma unroll
-          for (int d = 0; d < NDB; ++d) acc[d] = mfma_bf16(tr_operand<D>(sK, 16 * ks + 8 * hf, d, lane), sop, acc[d]);
+          for (int d = 0; d < NDB; ++d) {
+            const u32x2 klo = tr16(cur + offK[d][0] + ks * 16 * 2 * D);
+            const u32x2 khi = tr16(cur + offK[d][1] + ks * 16 * 2 * D);
+            acc[d] = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{klo[0], klo[1], khi[0], khi[1]}), sop, acc[d]);
+          }
         }
       }
-      wait_vmem();
-      __syncthreads();
+      wait_vmem_keep<C::DMA_PER_STAGE>();
+      barrier_keep_vmem();
+    };
+    issue(jt0, sbuf0);
+    issue(min(jt0 + 1, jt1), sbuf1);
+    wait_vmem_keep<C::DMA_PER_STAGE>();
+    barrier_keep_vmem();
+    for (int jt = jt0; jt <= jt1; jt += 3) {
+      step(jt, sbuf0, sbuf2);
+      if (jt + 1 <= jt1) step(jt + 1, sbuf1, sbuf0);
+      if (jt + 2 <= jt1) step(jt + 2, sbuf2, sbuf1);
     }
+    // No copy into this workgroup's LDS may still be in flight when its waves end.
+    wait_vmem();
   }
 
   if (!row_ok) return;
@@ -1951,10 +2004,10 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
+  const unsigned grid = (unsigned)((int64_t)((a.lq + DQS_ROWS - 1) / DQS_ROWS) * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
-  if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_ds_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL((bwd_dq_ds_kernel<64>), dim3(grid), dim3(NT), 0, s, a);
+  if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_ds_kernel<128>), dim3(grid), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((bwd_dq_ds_kernel<64>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
