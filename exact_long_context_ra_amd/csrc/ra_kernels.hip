@@ -984,6 +984,32 @@ __device__ __forceinline__ void dma_tile(Rsrc rs, uint32_t st, int r0, char* til
                                              (uint32_t)(r0 + row) * st + c * 16, 0, 0, 0);
   }
 }
+// The same copy with the per-lane part of every offset derived from two
+// registers: the swizzle is linear in the row bits and a wave's rows start at a
+// multiple of the rows one instruction covers, so the chunk of instruction i is
+// cx ^ swz(i * RPI) with cx = (lane mod CPR) ^ swz(lane / CPR), and the row
+// part splits into lane_row * st plus a wave-uniform scalar offset.
+// `cx16` = 16 * cx and `lrow_st` = (lane / CPR) * st come from dma_lane_parts().
+template <int D>
+__device__ __forceinline__ void dma_lane_parts(int lane, uint32_t st, uint32_t& cx16, uint32_t& lrow_st) {
+  constexpr int CPR = (2 * D) / 16;
+  cx16 = (uint32_t)(((lane % CPR) ^ swz<D>(lane / CPR)) << 4);
+  lrow_st = (uint32_t)(lane / CPR) * st;
+}
+template <int D, int ROWS, int NWAVES = 4>
+__device__ __forceinline__ void dma_tile_lean(Rsrc rs, uint32_t st, int r0, char* tile, int w, uint32_t cx16,
+                                              uint32_t lrow_st) {
+  constexpr int RPI = 1024 / (2 * D);
+  constexpr int RPW = ROWS / NWAVES;
+  static_assert(RPW % RPI == 0 && RPW % 16 == 0, "wave rows must start at a swizzle period");
+#pragma unroll
+  for (int i = 0; i < RPW / RPI; ++i) {
+    const int rbase = w * RPW + i * RPI;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + rbase * 2 * D), 16,
+                                             lrow_st + (cx16 ^ (uint32_t)(swz<D>(i * RPI) << 4)),
+                                             (uint32_t)(r0 + rbase) * st, 0, 0);
+  }
+}
 // Wait for this wave's outstanding global/buffer loads (including buffer->LDS).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait until at most N of this wave's vector-memory operations are outstanding
@@ -1005,96 +1031,30 @@ __device__ __forceinline__ void dma_f32x64(Rsrc rs, int first, char* dst, int la
 }
 
 // ============================================================================================
-// bf16 forward: tiles of 64 keys, K and V DMA'd one tile ahead into the other
-// of two LDS buffers; one barrier per tile.
+// bf16 forward, software-pipelined over tiles of 64 keys: while a wave turns
+// S of tile j into P (exponentials) and adds P V into O, it already issues the
+// MFMAs of S for tile j + 1, so that the matrix unit has work during the
+// softmax.  K tiles are therefore DMA'd two tiles ahead and V tiles one ahead,
+// each into the other of two LDS buffers; one barrier per tile.
 // ============================================================================================
 
 template <int D>
 struct FwdB {
   static constexpr int TILE = FBK * D * 2;  // bytes of one K (or V) tile
-  static constexpr int BUF = 2 * TILE;      // K then V
-  static constexpr int LDS = 2 * BUF;
 };
-
-template <int D>
-__device__ __forceinline__ void fwd_tile_bf16(const FwdArgs& a, int j0, const char* sK, const char* sV,
-                                              const bf16x8* qf, const Bounds& rb, const Bounds& wv_f,
-                                              const Bounds& wv_l, bool wave_has_rows, float& m_run, float& l_run,
-                                              f32x16* o, int lane, int l32, int hf) {
-  constexpr int NDB = D / 32;
-  const int jl = min(a.lk, j0 + FBK) - 1;
-  const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
-  if (!wave_has_rows || kmax < wv_f.lo || kmin > wv_l.hi) return;  // nothing visible to this wave
-  const bool wave_full = (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
-  const float sl2 = a.scale_log2;
-
-  // S^T for the two 32-key halves of the tile, the two MFMA chains interleaved.
-  f32x16 st[2] = {f32x16{}, f32x16{}};
-  const int row = row_perm(l32);
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    st[0] = mfma_bf16(row_operand<D>(sK, row, c, hf), qf[c], st[0]);
-    st[1] = mfma_bf16(row_operand<D>(sK, 32 + row, c, hf), qf[c], st[1]);
-  }
-  if (!wave_full) {
-    const bool in0 = j0 < a.kmap.s0.len;
-    const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
-    const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = j0 + c2 * 32 + reg_row(v, hf);
-        const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
-        const bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
-        st[c2][v] = ok ? st[c2][v] : NEG_INF;
-      }
-  }
-  float mx = NEG_INF;
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-  const bool grow = mx > m_run + RESCALE_TH;
-  if (__any(grow)) {
-    const float m_new = grow ? mx : m_run;
-    const float alpha = (m_new == m_run) ? 1.f : ex2(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) o[d] *= alpha;
-    m_run = m_new;
-  }
-  const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
-  float rs = 0.f;
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = ex2(__builtin_fmaf(st[c2][v], sl2, -m_use));
-      st[c2][v] = p;
-      rs += p;
-    }
-  l_run += rs;
-  // O^T += V^T P^T (V^T through the transposed read of the natural V tile)
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
-      const int key0 = c2 * 32 + 16 * u + 8 * hf;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) o[d] = mfma_bf16(tr_operand<D>(sV, key0, d, lane), pb, o[d]);
-    }
-}
 
 template <int D>
 __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
   using C = FwdB<D>;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  // Two K and two V buffers, four LDS objects: every read addresses one of
+  // them through one register plus an immediate, which lets the compiler see
+  // that a read does not touch the buffer a DMA is filling (it would
+  // otherwise wait for every copy in flight before the read).
+  __shared__ __attribute__((aligned(16))) char k_buf0[C::TILE];
+  __shared__ __attribute__((aligned(16))) char k_buf1[C::TILE];
+  __shared__ __attribute__((aligned(16))) char v_buf0[C::TILE];
+  __shared__ __attribute__((aligned(16))) char v_buf1[C::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1131,30 +1091,157 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
   const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
   const int kbeg = first_ge(a.kmap, wg_f.lo);
   const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+  const float sl2 = a.scale_log2;
 
-  float m_run = NEG_INF, l_run = 0.f;
+  float m_run = NEG_INF, l_run = 0.f, m_use = 0.f;
   f32x16 o[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) o[d] = f32x16{};
 
+  // Per-lane byte offsets of the LDS operand reads within a tile: K row krow
+  // (row_perm order), 16-byte chunk 2c + hf (row krow + 32 sits 32 rows, an
+  // immediate, further: the swizzle depends on the row modulo 16 only); and
+  // the transposed V reads of key rows 8*hf + (j >> 2) + 4*hi (j = lane mod 16)
+  // at column 32*d + 16*g1 + 4*(j & 3), g1 = bit 4 of the lane (key rows 16*m
+  // further are immediates too).
+  const int krow = row_perm(l32);
+  int offK[D / 16], offV[NDB][2];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) offK[c] = nat_off<D>(krow, 2 * c + hf);
+  {
+    const int j = lane & 15, g1 = (lane >> 4) & 1;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int colb = 2 * (32 * d + 16 * g1 + 4 * (j & 3));
+        offV[d][hi] = nat_off<D>(8 * hf + (j >> 2) + 4 * hi, colb >> 4) + (colb & 15);
+      }
+  }
+  // S^T of one tile (keys x this wave's rows) for the two 32-key halves, the
+  // two MFMA chains interleaved.
+  auto s_tile = [&](const char* sK, f32x16* st) {
+    st[0] = f32x16{};
+    st[1] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      st[0] = mfma_bf16(ld_bf16x8(sK + offK[c]), qf[c], st[0]);
+      st[1] = mfma_bf16(ld_bf16x8(sK + offK[c] + 32 * 2 * D), qf[c], st[1]);
+    }
+  };
+  // Visibility of tile jt's S^T for this wave's rows (-inf where a query row
+  // does not see a key), then the running maximum: O and the row sum are
+  // rescaled only when a row's maximum grows by more than RESCALE_TH (so that
+  // every P stays below 2^RESCALE_TH); the result is exact either way.
+  auto mask_max = [&](int jt, f32x16* st) {
+    const int j0 = jt * FBK;
+    const int jl = min(a.lk, j0 + FBK) - 1;
+    const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
+    const bool vis = wave_has_rows && kmax >= wv_f.lo && kmin <= wv_l.hi;
+    const bool full = vis && (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
+    if (!full) {
+      const bool in0 = j0 < a.kmap.s0.len;
+      const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
+      const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = j0 + c2 * 32 + reg_row(v, hf);
+          const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
+          const bool ok = vis && (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+          st[c2][v] = ok ? st[c2][v] : NEG_INF;
+        }
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const bool grow = mx > m_run + RESCALE_TH;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : ex2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) o[d] *= alpha;
+      m_run = m_new;
+    }
+    m_use = (m_run == NEG_INF) ? 0.f : m_run;
+  };
+  // P = exp2(S * scale*log2(e) - m) for the finished tile, its row sums, and
+  // O^T += V^T P^T (V^T through the transposed read of the natural V tile).
+  auto p_v = [&](f32x16* st, const char* sV) {
+    float rs = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = ex2(__builtin_fmaf(st[c2][v], sl2, -m_use));
+        st[c2][v] = p;
+        rs += p;
+      }
+    l_run += rs;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
+        const int kb0 = (c2 * 32 + 16 * u) * 2 * D;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const u32x2 lo = tr16(sV + offV[d][0] + kb0), hi = tr16(sV + offV[d][1] + kb0);
+          o[d] = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, o[d]);
+        }
+      }
+  };
+
   if (kbeg < kend) {
     const int jt0 = kbeg / FBK, jt1 = (kend - 1) / FBK;
-    dma_tile<D, FBK>(rk, kst, jt0 * FBK, smem, w, lane);
-    dma_tile<D, FBK>(rv, vst, jt0 * FBK, smem + C::TILE, w, lane);
+    dma_tile<D, FBK>(rk, kst, jt0 * FBK, k_buf0, w, lane);
+    dma_tile<D, FBK>(rv, vst, jt0 * FBK, v_buf0, w, lane);
+    if (jt0 < jt1) dma_tile<D, FBK>(rk, kst, (jt0 + 1) * FBK, k_buf1, w, lane);
     wait_vmem();
     __syncthreads();
-    for (int jt = jt0; jt <= jt1; ++jt) {
-      const int cur = (jt - jt0) & 1;
-      const char* sK = smem + cur * C::BUF;
-      if (jt < jt1) {
-        char* nK = smem + (cur ^ 1) * C::BUF;
-        dma_tile<D, FBK>(rk, kst, (jt + 1) * FBK, nK, w, lane);
-        dma_tile<D, FBK>(rv, vst, (jt + 1) * FBK, nK + C::TILE, w, lane);
+    f32x16 sa[2], sb[2];
+    s_tile(k_buf0, sa);
+    mask_max(jt0, sa);
+    __syncthreads();  // K buffer 0 is refilled below
+    // Tile jt is finished from `cur` while S of tile jt + 1 goes into `nxt`.
+    // On the last tile the S MFMAs read a stale buffer and are discarded, so
+    // that the work between the barriers has no branch.
+    uint32_t cx16, lk_st, lv_st;
+    dma_lane_parts<D>(lane, kst, cx16, lk_st);
+    dma_lane_parts<D>(lane, vst, cx16, lv_st);
+    // Tile jt (even offset from jt0: K of jt + 1 in k_buf1, V of jt in v_buf0;
+    // odd: the other two) while V of jt + 1 and K of jt + 2 are fetched.
+    auto step = [&](int jt, f32x16* cur, f32x16* nxt, const char* sKn, const char* sV, char* dV, char* dK) {
+      // recomputed per tile (a few VALU) rather than held in registers
+      uint32_t c16 = cx16, lks = lk_st, lvs = lv_st;
+      asm volatile("" : "+v"(c16), "+v"(lks), "+v"(lvs));
+      // Past the end the last tile is fetched again into the free buffer, so
+      // that the copies stay in the block of MFMAs; there they are spread one
+      // per two MFMAs (all of a workgroup's copies at once queue up in the
+      // vector-memory path and hold the waves that issue them).
+      dma_tile_lean<D, FBK>(rv, vst, min(jt + 1, jt1) * FBK, dV, w, c16, lvs);
+      dma_tile_lean<D, FBK>(rk, kst, min(jt + 2, jt1) * FBK, dK, w, c16, lks);
+      s_tile(sKn, nxt);
+      p_v(cur, sV);
+#pragma unroll
+      for (int g = 0; g < 2 * (FBK / (1024 / (2 * D))) / 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one buffer->LDS copy
       }
-      fwd_tile_bf16<D>(a, jt * FBK, sK, sK + C::TILE, qf, rb, wv_f, wv_l, wave_has_rows, m_run, l_run, o, lane,
-                       l32, hf);
       wait_vmem();
-      __syncthreads();
+      if (jt + 1 <= jt1) mask_max(jt + 1, nxt);
+      barrier_keep_vmem();
+    };
+    for (int jt = jt0; jt <= jt1; jt += 2) {
+      step(jt, sa, sb, k_buf1, v_buf0, v_buf1, k_buf0);
+      if (jt + 1 <= jt1) step(jt + 1, sb, sa, k_buf0, v_buf1, v_buf0, k_buf1);
     }
   }
 
@@ -1265,8 +1352,6 @@ struct DkdvB {
   // address plus an immediate offset that fits the LDS instruction.
   static constexpr int OFF_K = 0;                 // this workgroup's K tile (BWD_BK rows)
   static constexpr int OFF_V = BWD_BK * D * 2;    // and its V tile
-  static constexpr int OFF_BUF = 2 * BWD_BK * D * 2;
-  static constexpr int LDS = OFF_BUF + NBUF * BUF;
 };
 
 // dK/dV kernel: 8 waves; wave (kg, qh) owns keys 32*kg.. of the workgroup's
@@ -1280,7 +1365,12 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = DkdvB<D>;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  // The K/V tiles and the two query-tile buffers are three LDS objects, each
+  // buffer reached statically: a read of one buffer then does not wait for
+  // the DMA filling the other (the compiler cannot otherwise tell them apart).
+  __shared__ __attribute__((aligned(16))) char kv_lds[2 * BWD_BK * D * 2];
+  __shared__ __attribute__((aligned(16))) char qbuf0[C::BUF];
+  __shared__ __attribute__((aligned(16))) char qbuf1[C::BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1327,10 +1417,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const Bounds cbf = col_bounds(a.mask, map_pos(a.kmap, min(kw0, k_last)));      // wave's first key
   const Bounds cbl = col_bounds(a.mask, map_pos(a.kmap, kw_last));               // wave's last key
 
-  dma_tile<D, BWD_BK, 8>(rk, kst, k_first, smem + C::OFF_K, w, lane);
-  dma_tile<D, BWD_BK, 8>(rv, vst, k_first, smem + C::OFF_V, w, lane);
-  const char* sK = smem + C::OFF_K;
-  const char* sV = smem + C::OFF_V;
+  dma_tile<D, BWD_BK, 8>(rk, kst, k_first, kv_lds + C::OFF_K, w, lane);
+  dma_tile<D, BWD_BK, 8>(rv, vst, k_first, kv_lds + C::OFF_V, w, lane);
+  const char* sK = kv_lds + C::OFF_K;
+  const char* sV = kv_lds + C::OFF_V;
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) {
@@ -1364,8 +1454,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
 
-  auto issue = [&](int qtile, int slot) {
-    char* nb = smem + C::OFF_BUF + slot * C::BUF;
+  auto issue = [&](int qtile, char* nb) {
     const int r0 = qtile * BQB;
     dma_tile<D, BQB, 8>(rq, qst, r0, nb, w, lane);
     dma_tile<D, BQB, 8>(rdo, dst, r0, nb + C::OFF_DO, w, lane);
@@ -1390,14 +1479,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   if (qt0 <= qt1) {
-    issue(qt0, 0);
+    issue(qt0, qbuf0);
     wait_vmem();
     __syncthreads();
-    for (int qt = qt0; qt <= qt1; ++qt) {
-      const int i = qt - qt0;
-      const char* buf = smem + C::OFF_BUF + (i & 1) * C::BUF;
+    // query tile qt from `buf` while tile qt + 1 is fetched into `nbuf`
+    auto step = [&](int qt, const char* buf, char* nbuf) {
       flush();
-      if (qt + 1 <= qt1) issue(qt + 1, (i + 1) & 1);
+      if (qt + 1 <= qt1) issue(qt + 1, nbuf);
       const char* sQ = buf;
       const char* sDO = buf + C::OFF_DO;
       const float* sLse = reinterpret_cast<const float*>(buf + C::OFF_LSE);
@@ -1484,6 +1572,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       pend_soff = (uint32_t)(ds_offset(32 * ds_kblock, rw0, a.ds_ld) * 2);
       wait_vmem();
       __syncthreads();
+    };
+    for (int qt = qt0; qt <= qt1; qt += 2) {
+      step(qt, qbuf0, qbuf1);
+      if (qt + 1 <= qt1) step(qt + 1, qbuf1, qbuf0);
     }
     flush();
   }
@@ -1492,7 +1584,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   // Add the two query halves of each key group: waves qh = 1 park dK^T / dV^T
   // in LDS (reusing the K/V tiles), waves qh = 0 add and write out.
-  float* red = reinterpret_cast<float*>(smem);  // 4 key groups x 64 lanes x 16*NDB floats
+  float* red = reinterpret_cast<float*>(kv_lds);  // 4 key groups x 64 lanes x 16*NDB floats
   constexpr int PER = 16 * NDB;
   float* dkr = reinterpret_cast<float*>(a.dk.ptr) + b * a.dk.sb + (int64_t)key * a.dk.st + head * a.dk.sh;
   float* dvr = reinterpret_cast<float*>(a.dv.ptr) + b * a.dv.sb + (int64_t)key * a.dv.st + head * a.dv.sh;
