@@ -985,10 +985,10 @@ __device__ __forceinline__ void dma_tile(Rsrc rs, uint32_t st, int r0, char* til
   }
 }
 // The same copy with the per-lane part of every offset derived from two
-// registers: the swizzle is linear in the row bits and a wave's rows start at a
-// multiple of the rows one instruction covers, so the chunk of instruction i is
-// cx ^ swz(i * RPI) with cx = (lane mod CPR) ^ swz(lane / CPR), and the row
-// part splits into lane_row * st plus a wave-uniform scalar offset.
+// registers: the swizzle is linear in the row bits and every instruction's
+// first row rbase is a multiple of the rows it covers, so its chunk is
+// cx ^ swz(rbase) (wave-uniform) with cx = (lane mod CPR) ^ swz(lane / CPR),
+// and the row part splits into lane_row * st plus a wave-uniform scalar offset.
 // `cx16` = 16 * cx and `lrow_st` = (lane / CPR) * st come from dma_lane_parts().
 template <int D>
 __device__ __forceinline__ void dma_lane_parts(int lane, uint32_t st, uint32_t& cx16, uint32_t& lrow_st) {
@@ -1001,12 +1001,12 @@ __device__ __forceinline__ void dma_tile_lean(Rsrc rs, uint32_t st, int r0, char
                                               uint32_t lrow_st) {
   constexpr int RPI = 1024 / (2 * D);
   constexpr int RPW = ROWS / NWAVES;
-  static_assert(RPW % RPI == 0 && RPW % 16 == 0, "wave rows must start at a swizzle period");
+  static_assert(RPW % RPI == 0, "wave rows must split into whole instructions");
 #pragma unroll
   for (int i = 0; i < RPW / RPI; ++i) {
-    const int rbase = w * RPW + i * RPI;
+    const int rbase = w * RPW + i * RPI;  // wave-uniform, a multiple of RPI
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + rbase * 2 * D), 16,
-                                             lrow_st + (cx16 ^ (uint32_t)(swz<D>(i * RPI) << 4)),
+                                             lrow_st + (cx16 ^ (uint32_t)(swz<D>(rbase) << 4)),
                                              (uint32_t)(r0 + rbase) * st, 0, 0);
   }
 }
