@@ -14,6 +14,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "ra.h"
@@ -627,6 +628,68 @@ static ra_tensor shift_rows(const ra_tensor& t, int64_t rows, size_t esz) {
   return u;
 }
 
+// Independent rings (the sequences of a per-sequence layout) run concurrently
+// on a few side streams, forked from and joined back into the caller's stream
+// with events: one sequence's launches are small, and one after another they
+// leave most of the GPU idle.  Each host thread keeps its own streams and
+// events per device (default priority, non-blocking), created on first use and
+// kept until the process ends.
+constexpr int kSideStreams = 4;
+struct SidePool {
+  bool ready = false;
+  hipStream_t st[kSideStreams];
+  hipEvent_t fork, join[kSideStreams];
+};
+
+static ra_status side_pool(SidePool** out) {
+  static thread_local std::vector<SidePool> pools;
+  int dev = 0;
+  RA_HIP(hipGetDevice(&dev));
+  if ((int)pools.size() <= dev) pools.resize(dev + 1);
+  SidePool& p = pools[dev];
+  if (!p.ready) {
+    for (int k = 0; k < kSideStreams; ++k) {
+      RA_HIP(hipStreamCreateWithFlags(&p.st[k], hipStreamNonBlocking));
+      RA_HIP(hipEventCreateWithFlags(&p.join[k], hipEventDisableTiming));
+    }
+    RA_HIP(hipEventCreateWithFlags(&p.fork, hipEventDisableTiming));
+    p.ready = true;
+  }
+  *out = &p;
+  return RA_OK;
+}
+
+// Side stream of every piece: longest first onto the least-loaded stream (work
+// taken as L^2), over `nstreams` streams.
+static std::vector<int> assign_pieces(const std::vector<Piece>& pieces, int nstreams) {
+  std::vector<int> order(pieces.size()), where(pieces.size(), 0);
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::sort(order.begin(), order.end(), [&](int x, int y) { return pieces[x].L > pieces[y].L; });
+  std::vector<double> load(nstreams, 0.0);
+  for (int i : order) {
+    int best = 0;
+    for (int k = 1; k < nstreams; ++k)
+      if (load[k] < load[best]) best = k;
+    where[i] = best;
+    load[best] += (double)pieces[i].L * (double)pieces[i].L;
+  }
+  return where;
+}
+
+static ra_status fork_streams(SidePool* p, int n, hipStream_t s) {
+  RA_HIP(hipEventRecord(p->fork, s));
+  for (int k = 0; k < n; ++k) RA_HIP(hipStreamWaitEvent(p->st[k], p->fork, 0));
+  return RA_OK;
+}
+
+static ra_status join_streams(SidePool* p, int n, hipStream_t s) {
+  for (int k = 0; k < n; ++k) {
+    RA_HIP(hipEventRecord(p->join[k], p->st[k]));
+    RA_HIP(hipStreamWaitEvent(s, p->join[k], 0));
+  }
+  return RA_OK;
+}
+
 // The forward ring of one piece: rows [row0, row0 + pc.L) of the local buffers;
 // lse rows at lse + row0 with head stride lse_sh.
 static ra_status ring_fwd_piece(const Piece& pc, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
@@ -697,12 +760,19 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
            "stride_rank must be >= 0 and keep 16-byte alignment");
   hipStream_t s = (hipStream_t)stream;
-  for (const Piece& pc : pieces) {
-    st = ring_fwd_piece(pc, base_layout(layout), world, rank, q_local, k_ring, v_ring, stride_rank, out, lse, L,
-                        out_lowp, s);
-    if (st != RA_OK) return st;
-  }
-  return RA_OK;
+  if (pieces.size() == 1)
+    return ring_fwd_piece(pieces[0], base_layout(layout), world, rank, q_local, k_ring, v_ring, stride_rank, out,
+                          lse, L, out_lowp, s);
+  SidePool* pool = nullptr;
+  if ((st = side_pool(&pool)) != RA_OK) return st;
+  const int ns = (int)std::min<size_t>(kSideStreams, pieces.size());
+  const std::vector<int> where = assign_pieces(pieces, ns);
+  if ((st = fork_streams(pool, ns, s)) != RA_OK) return st;
+  for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i)
+    st = ring_fwd_piece(pieces[i], base_layout(layout), world, rank, q_local, k_ring, v_ring, stride_rank, out, lse,
+                        L, out_lowp, pool->st[where[i]]);
+  const ra_status sj = join_streams(pool, ns, s);
+  return st != RA_OK ? st : sj;
 }
 
 // Workspace of ra_ring_bwd: delta [b, h, L] fp32 (rounded up to 256 bytes), then
@@ -740,13 +810,19 @@ size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int
   return (bytes + 255) & ~(size_t)255;
 }
 
+// Streams the pieces of a ring run on: the caller's alone for one piece, else
+// up to kSideStreams side streams.
+static int ring_streams(const std::vector<Piece>& pieces) {
+  return pieces.size() <= 1 ? 1 : (int)std::min<size_t>(kSideStreams, pieces.size());
+}
+
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
   const size_t base = ra_ring_workspace_min_bytes(prob, layout, world);
   if (base == 0) return 0;
   int64_t L = 0;
   std::vector<Piece> pieces;
   ring_common(prob, layout, world, 0, &L, &pieces);
-  return base + ds_bytes_max(pieces);
+  return base + (size_t)ring_streams(pieces) * ds_bytes_max(pieces);
 }
 
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
@@ -776,8 +852,12 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
            "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  // One dS^T region per stream when the workspace holds them all, else none
+  // (then dQ comes from the recompute kernel).
   const size_t dsb = ds_bytes_max(pieces);
-  uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
+  const int ns = ring_streams(pieces);
+  const bool store_ds = dsb > 0 && workspace_bytes >= need + (size_t)ns * dsb;
+  auto ds_region = [&](int k) { return store_ds ? (uint16_t*)((char*)workspace + need + (size_t)k * dsb) : nullptr; };
 
   float* delta = (float*)workspace;
   hipStream_t s = (hipStream_t)stream;
@@ -797,7 +877,14 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     return launch_zero(dqw, prob->batch, prob->heads, (int32_t)L, prob->head_dim, s);
   }));
   const ra_layout lay = base_layout(layout);
-  for (const Piece& pc : pieces) {
+  SidePool* pool = nullptr;
+  std::vector<int> where(pieces.size(), 0);
+  if (ns > 1) {
+    if ((st = side_pool(&pool)) != RA_OK) return st;
+    where = assign_pieces(pieces, ns);
+    if ((st = fork_streams(pool, ns, s)) != RA_OK) return st;
+  }
+  auto run_piece = [&](const Piece& pc, hipStream_t ps, uint16_t* dsT) -> ra_status {
     const ra_problem* pp = &pc.prob;
     const ra_tensor qp = shift_rows(q_local, pc.row0, esz), kp = shift_rows(k_ring, pc.row0, esz);
     const ra_tensor vp = shift_rows(v_ring, pc.row0, esz), dop = shift_rows(dout, pc.row0, esz);
@@ -817,11 +904,17 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
       a.lse_sh = L;
       a.dsT = dsT;
       a.ds_ld = ds_ld_of(pc.L);
-      ra_status st2 = launch_bwd_step(a, pp->head_dim, bf16, step, s);
+      ra_status st2 = launch_bwd_step(a, pp->head_dim, bf16, step, ps);
       if (st2 != RA_OK) return st2;
     }
-  }
-  return RA_OK;
+    return RA_OK;
+  };
+  if (pieces.empty()) return RA_OK;
+  if (ns == 1) return run_piece(pieces[0], s, ds_region(0));
+  for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i)
+    st = run_piece(pieces[i], pool->st[where[i]], ds_region(where[i]));
+  const ra_status sj = join_streams(pool, ns, s);
+  return st != RA_OK ? st : sj;
 }
 
 }  // extern "C"
