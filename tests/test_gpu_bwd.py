@@ -128,3 +128,44 @@ def test_ring_bwd(case, store_ds):
         check_grad(f64(dq), gq[:, opos], bf, what=f"dq r={r}")
     check_grad(f64(dk_ring), oracle.to_ring(gk, layout, N, cu), bf, what="dk (all ranks)")
     check_grad(f64(dv_ring), oracle.to_ring(gv, layout, N, cu), bf, what="dv (all ranks)")
+
+
+def test_ring_per_sequence_on_user_stream():
+    """The per-sequence layouts run their sequences' rings on side streams,
+    forked from and joined back into the caller's stream.  Called on a user
+    stream, with the results consumed on that stream before any device-wide
+    synchronisation, forward and backward (dS stored per side stream, and the
+    recompute path) give bit-identical results to a default-stream run."""
+    import torch
+    ra = _ra()
+    layout, S, N, H, D = "zigzag_varlen", 2048, 4, 2, 128
+    log(f"ring per-sequence on a user stream {layout} S={S}")
+    cu = varlen_cu_multiple(S, 2 * N)
+    q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=7, device="cpu", with_dout=True)
+    q, k, v, do = q.to(dev()), k.to(dev()), v.to(dev()), do.to(dev())
+    kr, idx = ring_from_global(k, layout, N, cu)
+    vr, _ = ring_from_global(v, layout, N, cu)
+    r = 1
+    ql = q.index_select(1, idx[r]).contiguous()
+    dol = do.index_select(1, idx[r]).contiguous()
+
+    def run(store_ds):
+        o, l, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True, cu_seqlens=cu)
+        dq, dk, dv = ra.ring_bwd(layout, N, r, ql, kr, vr, o, l, dol, causal=True, cu_seqlens=cu,
+                                 store_ds=store_ds)
+        sums = torch.stack([t.double().sum() for t in (o, l.clamp(min=-1e30), dq, dk, dv)])
+        return (o, l, dq, dk, dv), sums
+
+    for store_ds in (True, False):
+        ref, _ = run(store_ds)
+        torch.cuda.synchronize()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            got, sums = run(store_ds)
+        st.synchronize()
+        for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), got, ref):
+            assert torch.equal(a, b), f"{name} differs on a user stream (store_ds={store_ds})"
+        ref_sums = torch.stack([t.double().sum() for t in (ref[0], ref[1].clamp(min=-1e30), *ref[2:])])
+        assert torch.equal(sums, ref_sums), "results consumed on the user stream before the join completed"
+        torch.cuda.synchronize()
