@@ -742,6 +742,99 @@ static ra_status ring_fwd_piece(const Piece& pc, ra_layout layout, int32_t world
   return RA_OK;
 }
 
+// Ring schedule of every piece of a per-sequence layout: its posmaps and, per
+// step, whether any pair is visible (a piece without any visible pair still
+// runs step 0, which writes its (0, -inf) rows).
+struct PiecePlan {
+  ra_posmap qmap;
+  std::vector<ra_posmap> kmap;  // per step
+  std::vector<char> active;     // per step
+  int first = -1, last = -1;    // first and last active step
+  bool forced = false;          // no visible pair at all: step 0 only writes (0, -inf)
+};
+
+static std::vector<PiecePlan> plan_pieces(const std::vector<Piece>& pieces, ra_layout lay, int32_t world,
+                                          int32_t rank) {
+  std::vector<PiecePlan> plans(pieces.size());
+  for (size_t i = 0; i < pieces.size(); ++i) {
+    const Piece& pc = pieces[i];
+    PiecePlan& pl = plans[i];
+    make_posmap(lay, pc.prob.seq_len, world, rank, &pl.qmap);
+    pl.kmap.resize(world);
+    pl.active.assign(world, 0);
+    for (int st = 0; st < world; ++st) {
+      const int src = ((rank - st) % world + world) % world;
+      make_posmap(lay, pc.prob.seq_len, world, src, &pl.kmap[st]);
+      pl.active[st] = step_has_pairs(&pc.prob, pl.qmap, pc.L, pl.kmap[st], pc.L) ? 1 : 0;
+    }
+    for (int st = 0; st < world; ++st)
+      if (pl.active[st]) {
+        if (pl.first < 0) pl.first = st;
+        pl.last = st;
+      }
+    if (pl.first < 0) {
+      pl.active[0] = 1;
+      pl.first = pl.last = 0;
+      pl.forced = true;
+    }
+  }
+  return plans;
+}
+
+// The pieces active at `step`, in groups of at most kMaxPieces.
+static std::vector<std::vector<int>> step_groups(const std::vector<PiecePlan>& plans, int step,
+                                                 bool skip_forced = false) {
+  std::vector<std::vector<int>> groups;
+  for (size_t i = 0; i < plans.size(); ++i) {
+    if (!plans[i].active[step] || (skip_forced && plans[i].forced)) continue;
+    if (groups.empty() || (int)groups.back().size() == kMaxPieces) groups.emplace_back();
+    groups.back().push_back((int)i);
+  }
+  return groups;
+}
+
+// bf16 forward of a per-sequence layout: per ring step, one launch over every
+// sequence that has visible pairs at that step (a piece table in the kernel
+// arguments), instead of one small launch per sequence.
+static ra_status ring_fwd_grouped(const std::vector<Piece>& pieces, ra_layout layout, int32_t world, int32_t rank,
+                                  ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
+                                  ra_tensor out, float* lse, int64_t L, ra_tensor out_lowp, hipStream_t s) {
+  const ra_problem* prob = &pieces[0].prob;
+  const size_t esz = elem_size(prob->dtype);
+  const std::vector<PiecePlan> plans = plan_pieces(pieces, base_layout(layout), world, rank);
+  FwdArgs base{};
+  base.q = rd(q_local);
+  base.out = wr(out);
+  base.lse = lse;
+  base.lse_sh = L;
+  base.out_lowp = wr(out_lowp);
+  base.batch = prob->batch;
+  base.heads = prob->heads;
+  base.lq = base.lk = (int32_t)L;
+  base.mask = mask_of(prob);
+  base.scale_log2 = scale_of(prob) * 1.4426950408889634f;
+  for (int step = 0; step < world; ++step) {
+    const int src = ((rank - step) % world + world) % world;
+    for (const std::vector<int>& grp : step_groups(plans, step)) {
+      FwdArgs a = base;
+      a.k = offset_rd(k_ring, src * stride_rank, esz);
+      a.v = offset_rd(v_ring, src * stride_rank, esz);
+      a.g.n = (int32_t)grp.size();
+      for (size_t j = 0; j < grp.size(); ++j) {
+        const int i = grp[j];
+        a.g.row0[j] = (int32_t)pieces[i].row0;
+        a.g.len[j] = (int32_t)pieces[i].L;
+        a.g.flags[j] = (step != plans[i].first ? PIECE_MERGE : 0) |
+                       (step == plans[i].last && out_lowp.ptr ? PIECE_LOWP : 0);
+        a.g.qmap[j] = to_dmap(plans[i].qmap);
+        a.g.kmap[j] = to_dmap(plans[i].kmap[step]);
+      }
+      RA_HIP(timed(K_FWD, step, s, [&] { return launch_fwd(a, prob->head_dim, true, s); }));
+    }
+  }
+  return RA_OK;
+}
+
 ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
                       ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, float* lse,
                       ra_tensor out_lowp, void* stream) {
@@ -763,6 +856,10 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   if (pieces.size() == 1)
     return ring_fwd_piece(pieces[0], base_layout(layout), world, rank, q_local, k_ring, v_ring, stride_rank, out,
                           lse, L, out_lowp, s);
+  if (prob->dtype == RA_DTYPE_BF16)
+    return ring_fwd_grouped(pieces, layout, world, rank, q_local, k_ring, v_ring, stride_rank, out, lse, L,
+                            out_lowp, s);
+  // fp32 (the parity path): one ring per sequence, the rings on side streams
   SidePool* pool = nullptr;
   if ((st = side_pool(&pool)) != RA_OK) return st;
   const int ns = (int)std::min<size_t>(kSideStreams, pieces.size());
@@ -791,6 +888,18 @@ static size_t ds_bytes(const ra_problem* prob, int64_t Lp) {
   return (size_t)prob->batch * prob->heads * (size_t)slice;
 }
 
+// dS^T of every piece side by side, for a grouped backward (0 unless every
+// piece fits the stored-dS path).
+static size_t ds_bytes_sum(const std::vector<Piece>& pieces) {
+  size_t sum = 0;
+  for (const Piece& pc : pieces) {
+    const size_t b = ds_bytes(&pc.prob, pc.L);
+    if (b == 0) return 0;
+    sum += b;
+  }
+  return sum;
+}
+
 // Every piece must fit the stored-dS path for it to be used (0 otherwise).
 static size_t ds_bytes_max(const std::vector<Piece>& pieces) {
   size_t m = 0;
@@ -810,10 +919,10 @@ size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int
   return (bytes + 255) & ~(size_t)255;
 }
 
-// Streams the pieces of a ring run on: the caller's alone for one piece, else
-// up to kSideStreams side streams.
-static int ring_streams(const std::vector<Piece>& pieces) {
-  return pieces.size() <= 1 ? 1 : (int)std::min<size_t>(kSideStreams, pieces.size());
+// dS^T bytes of the stored-dS path: one piece's, or every piece's side by side
+// for the grouped launches of a per-sequence layout (bf16; fp32 stores none).
+static size_t ds_bytes_ring(const std::vector<Piece>& pieces) {
+  return pieces.size() > 1 ? ds_bytes_sum(pieces) : ds_bytes_max(pieces);
 }
 
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
@@ -822,7 +931,7 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t
   int64_t L = 0;
   std::vector<Piece> pieces;
   ring_common(prob, layout, world, 0, &L, &pieces);
-  return base + (size_t)ring_streams(pieces) * ds_bytes_max(pieces);
+  return base + ds_bytes_ring(pieces);
 }
 
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
@@ -852,12 +961,10 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
            "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-  // One dS^T region per stream when the workspace holds them all, else none
-  // (then dQ comes from the recompute kernel).
-  const size_t dsb = ds_bytes_max(pieces);
-  const int ns = ring_streams(pieces);
-  const bool store_ds = dsb > 0 && workspace_bytes >= need + (size_t)ns * dsb;
-  auto ds_region = [&](int k) { return store_ds ? (uint16_t*)((char*)workspace + need + (size_t)k * dsb) : nullptr; };
+  // The dS^T buffer when the workspace holds it, else none (then dQ comes from
+  // the recompute kernel).
+  const size_t dsb = ds_bytes_ring(pieces);
+  uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
 
   float* delta = (float*)workspace;
   hipStream_t s = (hipStream_t)stream;
@@ -877,6 +984,42 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     return launch_zero(dqw, prob->batch, prob->heads, (int32_t)L, prob->head_dim, s);
   }));
   const ra_layout lay = base_layout(layout);
+  if (pieces.empty()) return RA_OK;
+  if (pieces.size() > 1 && bf16) {
+    // Grouped: per ring step one dK/dV launch and one dQ launch over every
+    // sequence with visible pairs at that step; each sequence has its own
+    // dS^T region, side by side in the workspace.
+    const std::vector<PiecePlan> plans = plan_pieces(pieces, lay, world, rank);
+    std::vector<int64_t> ds_off(pieces.size(), 0);
+    for (size_t i = 1; i < pieces.size(); ++i)
+      ds_off[i] = ds_off[i - 1] + (int64_t)(ds_bytes(&pieces[i - 1].prob, pieces[i - 1].L) / 2);
+    const ra_problem* p0 = &pieces[0].prob;
+    for (int step = 0; step < world; ++step) {
+      const int src = ((rank - step) % world + world) % world;
+      for (const std::vector<int>& grp : step_groups(plans, step, true)) {
+        BwdArgs a;
+        bwd_args(p0, q_local, L, plans[grp[0]].qmap, offset_rd(k_ring, src * stride_rank, esz),
+                 offset_rd(v_ring, src * stride_rank, esz), L, plans[grp[0]].kmap[step], dout, lse, delta, wr(dq),
+                 offset_wr(dk_ring, src * stride_rank_grad, 4), offset_wr(dv_ring, src * stride_rank_grad, 4), &a);
+        a.lse_sh = L;
+        a.dsT = dsT;
+        a.g.n = (int32_t)grp.size();
+        for (size_t j = 0; j < grp.size(); ++j) {
+          const int i = grp[j];
+          a.g.row0[j] = (int32_t)pieces[i].row0;
+          a.g.len[j] = (int32_t)pieces[i].L;
+          a.g.qmap[j] = to_dmap(plans[i].qmap);
+          a.g.kmap[j] = to_dmap(plans[i].kmap[step]);
+          a.g.ds_off[j] = ds_off[i];
+          a.g.ds_ld[j] = ds_ld_of(pieces[i].L);
+        }
+        if ((st = launch_bwd_step(a, p0->head_dim, true, step, s)) != RA_OK) return st;
+      }
+    }
+    return RA_OK;
+  }
+  // one ring: on the caller's stream; fp32 sequences: one ring each on side streams
+  const int ns = pieces.size() <= 1 ? 1 : (int)std::min<size_t>(kSideStreams, pieces.size());
   SidePool* pool = nullptr;
   std::vector<int> where(pieces.size(), 0);
   if (ns > 1) {
@@ -909,10 +1052,9 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     }
     return RA_OK;
   };
-  if (pieces.empty()) return RA_OK;
-  if (ns == 1) return run_piece(pieces[0], s, ds_region(0));
+  if (ns == 1) return run_piece(pieces[0], s, dsT);
   for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i)
-    st = run_piece(pieces[i], pool->st[where[i]], ds_region(where[i]));
+    st = run_piece(pieces[i], pool->st[where[i]], nullptr);
   const ra_status sj = join_streams(pool, ns, s);
   return st != RA_OK ? st : sj;
 }

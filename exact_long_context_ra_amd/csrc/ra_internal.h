@@ -35,6 +35,25 @@ struct Tensor4W {
 
 enum FwdMode : int32_t { FWD_STORE = 0, FWD_MERGE = 1 };
 
+// Independent rings in one launch (the sequences of a per-sequence layout, all
+// at the same ring step).  Piece p is rows [row0[p], row0[p] + len[p]) of the
+// q/out/lse (and of every k/v block and gradient) buffers, with its own
+// posmaps; its workgroups are blocks [wg_begin[p], wg_begin[p+1]) of the grid,
+// a multiple of 8 per piece so that the XCD mapping holds within each piece
+// (blocks past the piece's own count return at once).  wg_begin is filled by
+// the launch function of each kernel (block counts differ per kernel).
+constexpr int kMaxPieces = 16;
+struct PieceTable {
+  int32_t n;  // 0: not a grouped launch
+  int32_t wg_begin[kMaxPieces + 1];
+  int32_t row0[kMaxPieces], len[kMaxPieces];
+  int32_t flags[kMaxPieces];  // forward: bit 0 merge into out/lse (else store), bit 1 write out_lowp
+  DMap qmap[kMaxPieces], kmap[kMaxPieces];
+  int64_t ds_off[kMaxPieces];  // backward: element offset of the piece's dS^T region
+  int64_t ds_ld[kMaxPieces];
+};
+constexpr int32_t PIECE_MERGE = 1, PIECE_LOWP = 2;
+
 struct FwdArgs {
   Tensor4 q, k, v;
   Tensor4W out;      // fp32
@@ -47,6 +66,7 @@ struct FwdArgs {
   float scale_log2;  // softmax_scale * log2(e)
   int32_t mode;      // FwdMode
   int32_t n_qtiles;
+  PieceTable g;      // grouped launch (bf16 kernel only), g.n = 0 otherwise
 };
 
 struct BwdArgs {
@@ -66,6 +86,7 @@ struct BwdArgs {
   // the dK/dV kernel when set; read by the dQ-from-dS kernel.
   uint16_t* dsT;
   int64_t ds_ld;
+  PieceTable g;      // grouped launch (bf16 kernels only), g.n = 0 otherwise
 };
 
 struct MergeArgs {

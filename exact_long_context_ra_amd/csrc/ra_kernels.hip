@@ -154,6 +154,58 @@ __device__ __forceinline__ int xcd_logical(int bid, int total) {
   return (bid & 7) * (total >> 3) + (bid >> 3);
 }
 
+// Block of a grouped launch (a table of independent rings, see PieceTable):
+// finds this block's piece, points the row-based tensors at its rows and sets
+// its lengths, posmaps and flags; bid/nblk become the block index and count
+// within the piece.  bf16 operands, fp32 outputs and accumulators.
+__device__ __forceinline__ int piece_of(const PieceTable& g, int x) {
+  int p = 0;
+  while (p + 1 < g.n && g.wg_begin[p + 1] <= x) ++p;
+  return p;
+}
+__device__ __forceinline__ void fwd_piece(const FwdArgs& ap, FwdArgs& a, int& bid, int& nblk) {
+  const PieceTable& g = ap.g;
+  const int p = piece_of(g, (int)blockIdx.x);
+  bid = (int)blockIdx.x - g.wg_begin[p];
+  nblk = g.wg_begin[p + 1] - g.wg_begin[p];
+  const int64_t r0 = g.row0[p];
+  const int f = g.flags[p];
+  a.q.ptr = reinterpret_cast<const char*>(ap.q.ptr) + r0 * ap.q.st * 2;
+  a.k.ptr = reinterpret_cast<const char*>(ap.k.ptr) + r0 * ap.k.st * 2;
+  a.v.ptr = reinterpret_cast<const char*>(ap.v.ptr) + r0 * ap.v.st * 2;
+  a.out.ptr = reinterpret_cast<char*>(ap.out.ptr) + r0 * ap.out.st * 4;
+  a.out_lowp.ptr = (f & PIECE_LOWP) ? reinterpret_cast<char*>(ap.out_lowp.ptr) + r0 * ap.out_lowp.st * 2 : nullptr;
+  a.lse = ap.lse + r0;
+  a.lq = a.lk = g.len[p];
+  a.qmap = g.qmap[p];
+  a.kmap = g.kmap[p];
+  a.mode = (f & PIECE_MERGE) ? FWD_MERGE : FWD_STORE;
+  a.n_qtiles = (g.len[p] + FWD_BQ - 1) / FWD_BQ;
+}
+__device__ __forceinline__ void bwd_piece(const BwdArgs& ap, BwdArgs& a, int& bid, int& nblk) {
+  const PieceTable& g = ap.g;
+  const int p = piece_of(g, (int)blockIdx.x);
+  bid = (int)blockIdx.x - g.wg_begin[p];
+  nblk = g.wg_begin[p + 1] - g.wg_begin[p];
+  const int64_t r0 = g.row0[p];
+  a.q.ptr = reinterpret_cast<const char*>(ap.q.ptr) + r0 * ap.q.st * 2;
+  a.k.ptr = reinterpret_cast<const char*>(ap.k.ptr) + r0 * ap.k.st * 2;
+  a.v.ptr = reinterpret_cast<const char*>(ap.v.ptr) + r0 * ap.v.st * 2;
+  a.dout.ptr = reinterpret_cast<const char*>(ap.dout.ptr) + r0 * ap.dout.st * 2;
+  a.dq.ptr = reinterpret_cast<char*>(ap.dq.ptr) + r0 * ap.dq.st * 4;
+  a.dk.ptr = reinterpret_cast<char*>(ap.dk.ptr) + r0 * ap.dk.st * 4;
+  a.dv.ptr = reinterpret_cast<char*>(ap.dv.ptr) + r0 * ap.dv.st * 4;
+  a.lse = ap.lse + r0;
+  a.delta = ap.delta + r0;
+  a.lq = a.lk = g.len[p];
+  a.qmap = g.qmap[p];
+  a.kmap = g.kmap[p];
+  a.n_ktiles = (g.len[p] + BWD_BK - 1) / BWD_BK;
+  a.n_qtiles = (g.len[p] + FWD_BQ - 1) / FWD_BQ;
+  a.dsT = ap.dsT ? ap.dsT + g.ds_off[p] : nullptr;
+  a.ds_ld = g.ds_ld[p];
+}
+
 // ============================================================================================
 // Buffer loads.  Each (batch, head) slice of a tensor gets a range-checked
 // buffer descriptor; a read past the slice returns zeros, so ragged tiles need
@@ -1044,7 +1096,10 @@ struct FwdB {
 };
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
+  FwdArgs a = ap;
+  int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
+  if (ap.g.n) fwd_piece(ap, a, bid, nblk);
   using C = FwdB<D>;
   constexpr int NDB = D / 32;
   // Two K and two V buffers, four LDS objects: every read addresses one of
@@ -1058,9 +1113,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int logical = xcd_logical(bid, nblk);
   const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;  // latest (heaviest causal) tiles first
   const int bh = logical / a.n_qtiles;
+  if (bh >= a.heads * a.batch) return;  // a grouped launch's padding block
   const int head = bh % a.heads, b = bh / a.heads;
 
   const int r_first = qt * FWD_BQ;
@@ -1362,7 +1418,10 @@ struct DkdvB {
 // the key's column interval (col_bounds), so no per-row lookups are needed.
 // The two query halves of a key group add their dK/dV through LDS at the end.
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
+  BwdArgs a = ap;
+  int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
+  if (ap.g.n) bwd_piece(ap, a, bid, nblk);
   using C = DkdvB<D>;
   constexpr int NDB = D / 32;
   // The K/V tiles and the two query-tile buffers are three LDS objects, each
@@ -1375,9 +1434,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = w & 3, qh = w >> 2;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int logical = xcd_logical(bid, nblk);
   const int kt = logical % a.n_ktiles;  // earliest (heaviest causal) key tiles first
   const int bh = logical / a.n_ktiles;
+  if (bh >= a.heads * a.batch) return;  // a grouped launch's padding block
   const int head = bh % a.heads, b = bh / a.heads;
 
   const char* qbase = reinterpret_cast<const char*>(a.q.ptr) + (b * a.q.sb + head * a.q.sh) * 2;
@@ -1643,16 +1703,20 @@ struct DqB {
 };
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs ap) {
+  BwdArgs a = ap;
+  int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
+  if (ap.g.n) bwd_piece(ap, a, bid, nblk);
   using C = DqB<D>;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int logical = xcd_logical(bid, nblk);
   const int qt = a.n_qtiles - 1 - logical % a.n_qtiles;
   const int bh = logical / a.n_qtiles;
+  if (bh >= a.heads * a.batch) return;  // a grouped launch's padding block
   const int head = bh % a.heads, b = bh / a.heads;
 
   const int r_first = qt * FWD_BQ;
@@ -1794,7 +1858,10 @@ struct DqsB {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
+  BwdArgs a = ap;
+  int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
+  if (ap.g.n) bwd_piece(ap, a, bid, nblk);
   using C = DqsB<D>;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char sbuf0[C::BUF];
@@ -1805,9 +1872,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = w >> 2, wcol = w & 3;  // this wave's dS^T sub-tile and its 32-row column block
   const int n_qt = (a.lq + DQS_ROWS - 1) / DQS_ROWS;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int logical = xcd_logical(bid, nblk);
   const int qt = n_qt - 1 - logical % n_qt;
   const int bh = logical / n_qt;
+  if (bh >= a.heads * a.batch) return;  // a grouped launch's padding block
   const int head = bh % a.heads, b = bh / a.heads;
 
   const int r_first = qt * DQS_ROWS;
@@ -2066,9 +2134,25 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 // Launchers
 // ============================================================================================
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
+// Grid of a grouped launch: each piece gets ceil(len / rows) x heads x batch
+// blocks, rounded up to a multiple of 8; fills g.wg_begin.
+static unsigned group_grid(PieceTable& g, int rows, int heads, int batch) {
+  int64_t acc = 0;
+  for (int p = 0; p < g.n; ++p) {
+    g.wg_begin[p] = (int32_t)acc;
+    const int64_t blocks = (int64_t)((g.len[p] + rows - 1) / rows) * heads * batch;
+    acc += (blocks + 7) / 8 * 8;
+  }
+  g.wg_begin[g.n] = (int32_t)acc;
+  return (unsigned)acc;
+}
+
+hipError_t launch_fwd(const FwdArgs& a0, int head_dim, bool bf16, hipStream_t s) {
+  FwdArgs a = a0;
+  const unsigned grid = a.g.n ? group_grid(a.g, FWD_BQ, a.heads, a.batch)
+                              : (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
+  if (a.g.n && !bf16) return hipErrorInvalidValue;  // only the bf16 kernel takes a piece table
   if (bf16) {
     if (head_dim == 128) hipLaunchKernelGGL((fwd_kernel_bf16<128>), dim3(grid), dim3(NT), 0, s, a);
     else hipLaunchKernelGGL((fwd_kernel_bf16<64>), dim3(grid), dim3(NT), 0, s, a);
@@ -2087,24 +2171,30 @@ hipError_t launch_bwd_fused_f32(const BwdArgs& a, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
+hipError_t launch_bwd_dkdv(const BwdArgs& a0, int head_dim, hipStream_t s) {
+  BwdArgs a = a0;
+  const unsigned grid = a.g.n ? group_grid(a.g, BWD_BK, a.heads, a.batch)
+                              : (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(512), 0, s, a);
   else hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)((a.lq + DQS_ROWS - 1) / DQS_ROWS) * a.heads * a.batch);
+hipError_t launch_bwd_dq_ds(const BwdArgs& a0, int head_dim, hipStream_t s) {
+  BwdArgs a = a0;
+  const unsigned grid = a.g.n ? group_grid(a.g, DQS_ROWS, a.heads, a.batch)
+                              : (unsigned)((int64_t)((a.lq + DQS_ROWS - 1) / DQS_ROWS) * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_ds_kernel<128>), dim3(grid), dim3(512), 0, s, a);
   else hipLaunchKernelGGL((bwd_dq_ds_kernel<64>), dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
+hipError_t launch_bwd_dq(const BwdArgs& a0, int head_dim, hipStream_t s) {
+  BwdArgs a = a0;
+  const unsigned grid = a.g.n ? group_grid(a.g, FWD_BQ, a.heads, a.batch)
+                              : (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
   else hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(NT), 0, s, a);

@@ -161,11 +161,13 @@ ra_status ra_block_attn_bwd(const ra_problem* prob,
  * attention kernel's epilogue (fp32 throughout); steps without any visible pair
  * are not launched.  With a *_VARLEN layout (cu_seqlens and its host copy
  * required) the sequences never attend to each other, so each sequence's rows
- * (a contiguous run of the local tokens) run as a ring of their own.  With more
- * than one sequence these rings run concurrently on up to 4 side streams that
- * the library creates per host thread and device on first use (default
- * priority, kept until the process ends), forked from `stream` and joined back
- * into it with events: the work is ordered on `stream` as if it ran there. */
+ * (a contiguous run of the local tokens) run as a ring of their own.  For bf16,
+ * each ring step is one launch over every sequence with visible pairs at that
+ * step (up to 16 sequences per launch).  For fp32 the sequences' rings run
+ * concurrently on up to 4 side streams that the library creates per host thread
+ * and device on first use (default priority, kept until the process ends),
+ * forked from `stream` and joined back into it with events: the work is
+ * ordered on `stream` as if it ran there. */
 ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
                       ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
                       ra_tensor out, float* lse, ra_tensor out_lowp, void* stream);
@@ -182,8 +184,8 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
  *  reaches ra_ring_workspace_bytes(), the bf16 dS^T of the current step: the dK/dV
  *  kernel then stores dS and dQ = dS K is one product per pair instead of a recompute
  *  of S, P and dP.  With less than that, dQ is computed by the recompute kernel.
- *  The per-sequence layouts run their sequences on side streams as ra_ring_fwd does,
- *  each stream with its own dS^T region. */
+ *  The per-sequence layouts run their sequences as ra_ring_fwd does (bf16: grouped
+ *  launches, every sequence with its own dS^T region side by side). */
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
                       ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
                       ra_tensor out, const float* lse, ra_tensor dout,
@@ -192,8 +194,8 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
 
 /* Bytes of device workspace for ra_ring_bwd's fastest path (0 on invalid input):
  * delta (b*h*L fp32) and, for bf16, dS^T (b*h*round_up(L, 128)^2 bf16), L = S/N;
- * for a per-sequence layout, one dS^T region per side stream (up to 4), each for
- * the longest sequence's local length in place of L.
+ * for a per-sequence layout, the sum of that dS^T size over the sequences, each
+ * with its own local length in place of L.
  * Never smaller than ra_ring_workspace_min_bytes(). */
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world);
 
