@@ -96,3 +96,13 @@ def varlen_cu_multiple(S: int, unit: int):
     rest = S - sum(lengths)
     assert rest > 0 and rest % unit == 0
     return synth.cu_seqlens(lengths + [rest])
+
+
+def varlen_cu_many(S: int, unit: int, n: int = 21):
+    """cu_seqlens of n packed sequences (more than one grouped launch holds),
+    lengths multiples of `unit` from 1 to 11 units, the rest of S last."""
+    import synth
+    lengths = [unit * (1 + (i * 7) % 11) for i in range(n - 1)]
+    rest = S - sum(lengths)
+    assert rest > 0 and rest % unit == 0
+    return synth.cu_seqlens(lengths + [rest])

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_lse, check_out, dev, f64, log, ring_from_global, varlen_cu_multiple
+from gpu_util import check_lse, check_out, dev, f64, log, ring_from_global, varlen_cu_many, varlen_cu_multiple
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +109,7 @@ RING_CASES = [
     ("zigzag_varlen", 1536, 4, 2, 64, "f32", True, "varlen", 1),
     ("stripe_varlen", 1536, 4, 2, 128, "f32", True, "varlen", 1),
     ("stripe_varlen", 2048, 8, 2, 64, "bf16", True, "varlen", 1),
+    ("stripe_varlen", 2048, 4, 2, 128, "bf16", True, "many", 1),   # 21 sequences: two grouped launches
 ]
 
 
@@ -125,7 +126,9 @@ def test_ring_fwd(case):
     ra = _ra()
     layout, S, N, H, D, dt, causal, cu, B = case
     log(f"ring_fwd {case}")
-    if cu == "varlen":
+    if cu == "many":
+        cu = varlen_cu_many(S, 2 * N if layout == "zigzag_varlen" else N)
+    elif cu == "varlen":
         per_seq = layout.endswith("_varlen")
         cu = varlen_cu_multiple(S, 2 * N if layout == "zigzag_varlen" else N) if per_seq else _varlen_cu(S)
     seed = 0 if S == 512 else 11
