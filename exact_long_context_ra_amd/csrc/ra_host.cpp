@@ -880,11 +880,12 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
 static int64_t ds_ld_of(int64_t L) { return (L + FWD_BQ - 1) / FWD_BQ * FWD_BQ; }
 
 // dS^T bytes of a piece of Lp local rows, or 0 where the stored-dS path does
-// not apply (fp32, or one (b, h) slice too large for 32-bit buffer offsets).
+// not apply (fp32, or one (b, h) slice beyond the 32-bit byte offsets of a
+// buffer descriptor: Lp above 46336).
 static size_t ds_bytes(const ra_problem* prob, int64_t Lp) {
   if (prob->dtype != RA_DTYPE_BF16 || Lp == 0) return 0;
   const int64_t slice = (Lp + BWD_BK - 1) / BWD_BK * BWD_BK * ds_ld_of(Lp) * 2;
-  if (slice >= ((int64_t)1 << 31)) return 0;
+  if (slice >= ((int64_t)1 << 32)) return 0;
   return (size_t)prob->batch * prob->heads * (size_t)slice;
 }
 

@@ -1524,18 +1524,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
 
   // dS^T of a tile is stored at the start of the next one: the wait at the end
   // of a tile covers every memory operation of the wave (stores included), and
-  // a store issued a whole tile earlier has completed by then.  A pending store
-  // with nothing to write gets an offset past any buffer (2^31: the descriptor
-  // is smaller, and adding the scalar offset does not wrap) and is dropped.
-  constexpr uint32_t kNoStore = 0x80000000u;
+  // a store issued a whole tile earlier has completed by then.  A wave with
+  // nothing pending (no rows in the tile, or before the first tile) stores
+  // through a descriptor of size 0, so the stores are dropped (the choice is
+  // wave-uniform, so offsets may span the whole 32-bit range of a slice).
   constexpr int kNonTemporal = 2;  // cache-policy bit: dS^T streams out, no reuse before the dQ kernel
+  const Rsrc rds_none = make_rsrc(a.dsT, 0u);
   bf16x8 pend[2] = {zero_bf16x8(), zero_bf16x8()};
-  uint32_t pend_voff = kNoStore, pend_soff = 0;
+  bool pend_live = false;
+  uint32_t pend_soff = 0;
   auto flush = [&]() {
+    const Rsrc rs = pend_live ? rds : rds_none;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pend[u]), rds, pend_voff,
-                                             pend_soff + 1024 * u, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pend[u]), rs, ds_voff, pend_soff + 1024 * u,
+                                             kNonTemporal);
   };
 
   if (qt0 <= qt1) {
@@ -1628,7 +1631,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
         pend[0] = zero_bf16x8();
         pend[1] = zero_bf16x8();
       }
-      pend_voff = rw0 <= rwl ? ds_voff : kNoStore;
+      pend_live = rw0 <= rwl;
       pend_soff = (uint32_t)(ds_offset(32 * ds_kblock, rw0, a.ds_ld) * 2);
       wait_vmem();
       __syncthreads();
