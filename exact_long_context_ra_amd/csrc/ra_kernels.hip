@@ -1943,7 +1943,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
         const int c = (lane & 15) ^ swz<128>(kr);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (lds_void*)(buf + C::KT + sub * C::ST + (8 * w + 4 * i) * 256), 16,
-            (uint32_t)(ds_offset(jt * DQ_BK + kr, r_first + 128 * sub + 8 * c, a.ds_ld) * 2), 0, 0, 0);
+            (uint32_t)(ds_offset(jt * DQ_BK + kr, r_first + 128 * sub + 8 * c, a.ds_ld) * 2), 0, 0,
+            2 /* non-temporal: dS^T is read once */);
       }
   };
 
