@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 H, D = 32, 128
 HEADS = [0, 17, 31]
+TAIL_REL = 3e-2
 
 
 def _ra():
@@ -85,6 +86,41 @@ def _check_dq_rows(q, do, dq, out_rows_ref, lse_rows_ref, pos, rows, k64, v64, h
     check_grad(f64(dq.index_select(2, hsel))[:, rows], gq, True, what=f"{what} dq")
 
 
+def _check_tail_dkdv(q, do, dk_ring, dv_ring, pos, idx, k64, v64, hsel, what, tail=96):
+    """Exact dK/dV for the keys that only the share's last `tail` query rows
+    (by position) see: under the causal mask a key at position p is seen by the
+    rows at positions >= p, so for every key past the position of the
+    (tail+1)-th last row all of its viewers are among those rows, and the
+    oracle needs the forward of those rows alone.  dk_ring/dv_ring hold this
+    rank's contributions only."""
+    import torch
+    S = k64.shape[1]
+    order = np.argsort(pos)
+    rows = np.sort(order[-tail:])
+    thr = int(pos[order[-tail - 1]])
+    kpos = np.arange(thr + 1, int(pos.max()) + 1)
+    gidx = torch.from_numpy(pos[rows]).to(q.device)
+    qr = f64(q.index_select(2, hsel).index_select(1, gidx))
+    dor = f64(do.index_select(2, hsel).index_select(1, gidx))
+    ro, rl = oracle.attention(qr, k64, v64, pos[rows], np.arange(S), True)
+    _, gk, gv = oracle.attention_backward(qr, k64[:, kpos], v64[:, kpos], ro, rl, dor, pos[rows], kpos, True)
+    # global position -> row of the rank-major ring
+    inv = np.empty(S, dtype=np.int64)
+    inv[torch.cat(idx).cpu().numpy()] = np.arange(S)
+    ring_rows = torch.from_numpy(inv[kpos]).to(q.device)
+    N, B, L = dk_ring.shape[:3]
+    got_k = f64(dk_ring.reshape(N * L, *dk_ring.shape[3:]).index_select(0, ring_rows).index_select(1, hsel))[None]
+    got_v = f64(dv_ring.reshape(N * L, *dv_ring.shape[3:]).index_select(0, ring_rows).index_select(1, hsel))[None]
+    # These gradients are sums over a few rows, far below 1 in magnitude, so the
+    # bound is relative to their own largest value: bf16 P and dS carry 2^-9
+    # relative rounding per term, and TAIL_REL leaves room for cancellation.
+    for name, got, ref in (("dk", got_k, gk), ("dv", got_v, gv)):
+        mx = float(np.max(np.abs(ref)))
+        rel = float(np.max(np.abs(got - ref))) / mx
+        log(f"{what}: {name} of {len(kpos)} keys seen only by the last {tail} rows: max err {rel:.2e} of max|ref|")
+        assert rel <= TAIL_REL, f"{what} {name} tail: max abs err {rel:.3e} of max|ref| {mx:.3e} > {TAIL_REL}"
+
+
 @pytest.mark.parametrize("layout,S,rank", [("zigzag", 131072, 0), ("zigzag", 131072, 5),
                                            ("stripe", 262144, 0)])
 def test_full_size_fwd_bwd(layout, S, rank):
@@ -109,6 +145,7 @@ def test_full_size_fwd_bwd(layout, S, rank):
     _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, None, f"{layout} r{rank}")
     has = torch.ones(L, device=dev(), dtype=torch.float64)  # causal self-attention: every row sees itself
     _check_invariants(dk_ring, dv_ring, dol, has, f"{layout} r{rank}")
+    _check_tail_dkdv(q, do, dk_ring, dv_ring, pos, idx, k64, v64, hsel, f"{layout} r{rank}")
 
 
 def test_full_size_contiguous_all_ranks():
