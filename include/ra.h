@@ -13,14 +13,21 @@
  * this GPU, with every rank's K/V block resident in device memory.
  *
  * Conventions (apply to every entry point):
- *  - Every call returns ra_status.  On any non-OK status nothing has been
- *    enqueued and no output has been written; ra_last_error() returns a
- *    thread-local message describing the failure.
+ *  - Every call returns ra_status.  Arguments are validated before anything is
+ *    enqueued: on RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED or RA_ERR_WORKSPACE
+ *    nothing has been enqueued and no output written.  RA_ERR_HIP reports a
+ *    failed launch, after which launches enqueued before it may still run.
+ *    ra_last_error() returns a thread-local message describing the failure.
  *  - Tensors are caller-owned DEVICE memory.  The library never allocates or
  *    frees device memory; calls that need scratch take a caller workspace.
  *  - Calls are asynchronous on the caller's stream (a hipStream_t passed as
  *    void*, NULL = the null stream).  Buffers must stay alive and unmodified
- *    until the stream has finished the work.
+ *    until the stream has finished the work.  A call enqueues kernel launches
+ *    only (plus event record/wait for the fp32 per-sequence rings), with no
+ *    allocation, memset or synchronisation, so it may be captured into a HIP
+ *    graph and replayed; kernel timing (ra_timing_begin) must be off then, and
+ *    the fp32 per-sequence rings need one eager call on the thread first (it
+ *    creates their side streams and events).
  *  - Q/K/V/dO and outputs are token-major [batch, tokens, heads, head_dim]
  *    described by ra_tensor: element strides for batch, token and head; the
  *    head_dim axis is contiguous.  Base pointers and all strides must keep
