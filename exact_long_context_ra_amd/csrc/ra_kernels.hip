@@ -1647,18 +1647,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
 
   // Add the two query halves of each key group: waves qh = 1 park dK^T / dV^T
   // in LDS (reusing the K/V tiles), waves qh = 0 add and write out.
-  float* red = reinterpret_cast<float*>(kv_lds);  // 4 key groups x 64 lanes x 16*NDB floats
+  // Per key group, 4*NDB rows of 64 lanes x 16 bytes: the lanes of one access
+  // sit side by side, so a wave's 16-byte writes and reads are conflict free.
+  float* red = reinterpret_cast<float*>(kv_lds);  // 4 key groups x 4*NDB x 64 lanes x 4 floats
   constexpr int PER = 16 * NDB;
   float* dkr = reinterpret_cast<float*>(a.dk.ptr) + b * a.dk.sb + (int64_t)key * a.dk.st + head * a.dk.sh;
   float* dvr = reinterpret_cast<float*>(a.dv.ptr) + b * a.dv.sb + (int64_t)key * a.dv.st + head * a.dv.sh;
-  float* slot = red + (kg * 64 + lane) * PER;
+  float* slot = red + kg * 64 * PER + lane * 4;  // group q = 4d + g at slot + q * 256
   // pass 0: dK (scaled), pass 1: dV
   if (qh == 1) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(slot + 16 * d + 4 * g) =
+        *reinterpret_cast<f32x4*>(slot + (4 * d + g) * 256) =
             f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]};
   }
   __syncthreads();
@@ -1668,7 +1670,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = d * 32 + 8 * g + 4 * hf;
-        const f32x4 other = *reinterpret_cast<const f32x4*>(slot + 16 * d + 4 * g);
+        const f32x4 other = *reinterpret_cast<const f32x4*>(slot + (4 * d + g) * 256);
         f32x4 x = *reinterpret_cast<const f32x4*>(dkr + d0);
         x += a.scale * (f32x4{dk[d][4 * g], dk[d][4 * g + 1], dk[d][4 * g + 2], dk[d][4 * g + 3]} + other);
         *reinterpret_cast<f32x4*>(dkr + d0) = x;
@@ -1680,7 +1682,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(slot + 16 * d + 4 * g) =
+        *reinterpret_cast<f32x4*>(slot + (4 * d + g) * 256) =
             f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]};
   }
   __syncthreads();
@@ -1690,7 +1692,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = d * 32 + 8 * g + 4 * hf;
-        const f32x4 other = *reinterpret_cast<const f32x4*>(slot + 16 * d + 4 * g);
+        const f32x4 other = *reinterpret_cast<const f32x4*>(slot + (4 * d + g) * 256);
         f32x4 y = *reinterpret_cast<const f32x4*>(dvr + d0);
         y += f32x4{dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]} + other;
         *reinterpret_cast<f32x4*>(dvr + d0) = y;
