@@ -781,14 +781,21 @@ static std::vector<PiecePlan> plan_pieces(const std::vector<Piece>& pieces, ra_l
   return plans;
 }
 
-// The pieces active at `step`, in groups of at most kMaxPieces.
-static std::vector<std::vector<int>> step_groups(const std::vector<PiecePlan>& plans, int step,
+// The pieces active at `step`, longest first, in groups of at most kMaxPieces.
+// Workgroups are dispatched roughly in id order and a longer piece has the
+// longer-running workgroups, so putting it first keeps them off the end of the
+// launch.
+static std::vector<std::vector<int>> step_groups(const std::vector<Piece>& pieces,
+                                                 const std::vector<PiecePlan>& plans, int step,
                                                  bool skip_forced = false) {
+  std::vector<int> order(plans.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return pieces[x].L > pieces[y].L; });
   std::vector<std::vector<int>> groups;
-  for (size_t i = 0; i < plans.size(); ++i) {
+  for (int i : order) {
     if (!plans[i].active[step] || (skip_forced && plans[i].forced)) continue;
     if (groups.empty() || (int)groups.back().size() == kMaxPieces) groups.emplace_back();
-    groups.back().push_back((int)i);
+    groups.back().push_back(i);
   }
   return groups;
 }
@@ -815,7 +822,7 @@ static ra_status ring_fwd_grouped(const std::vector<Piece>& pieces, ra_layout la
   base.scale_log2 = scale_of(prob) * 1.4426950408889634f;
   for (int step = 0; step < world; ++step) {
     const int src = ((rank - step) % world + world) % world;
-    for (const std::vector<int>& grp : step_groups(plans, step)) {
+    for (const std::vector<int>& grp : step_groups(pieces, plans, step)) {
       FwdArgs a = base;
       a.k = offset_rd(k_ring, src * stride_rank, esz);
       a.v = offset_rd(v_ring, src * stride_rank, esz);
@@ -997,7 +1004,7 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     const ra_problem* p0 = &pieces[0].prob;
     for (int step = 0; step < world; ++step) {
       const int src = ((rank - step) % world + world) % world;
-      for (const std::vector<int>& grp : step_groups(plans, step, true)) {
+      for (const std::vector<int>& grp : step_groups(pieces, plans, step, true)) {
         BwdArgs a;
         bwd_args(p0, q_local, L, plans[grp[0]].qmap, offset_rd(k_ring, src * stride_rank, esz),
                  offset_rd(v_ring, src * stride_rank, esz), L, plans[grp[0]].kmap[step], dout, lse, delta, wr(dq),
