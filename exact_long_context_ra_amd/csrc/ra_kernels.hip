@@ -1578,6 +1578,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
           s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), row_operand<D>(sK, 32 * kg + l32, c, hf), s);
           dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), row_operand<D>(sV, 32 * kg + l32, c, hf), dp);
         }
+        // The four operand reads of a k-step are issued one k-step ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int c = 0; c < D / 16 - 2; ++c) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // P and dS per half u of this lane's 16 rows (rows hr0 + 16u + 8hf + i2),
         // packed to bf16 as they are made; lse (to base 2) and delta of the
         // 8 rows come as two 16-byte reads each.  Fully visible blocks take a
@@ -1623,6 +1631,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
             dv[d] = mfma_bf16(tr_op(sDO, u, d), pb, dv[d]);
             dk[d] = mfma_bf16(tr_op(sQ, u, d), sb, dk[d]);
           }
+          // the transposed reads of a pair of products are issued one pair ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int d = 0; d < NDB - 2; ++d) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
       }
       // This tile's block of dS^T is stored with the next tile; blocks that
