@@ -45,6 +45,7 @@ constexpr float POS_INF = __builtin_huge_valf();
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int INT_BIG = 0x7fffffff;
+constexpr float FLT_MAX_F = 3.40282347e+38f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -1586,59 +1587,69 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        // Blocks that are not fully visible set the scores of invisible
+        // (query, key) pairs to -inf first; what follows is the same
+        // straight-line code for every tile.
+        if (!wave_full) {
+          int hq = 8 * hf;
+          asm volatile("" : "+v"(hq));  // keeps the 16 row indices from being precomputed
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qm = hr0 + 16 * (v >> 3) + hq + (v & 7);
+            const int r = qt * BQB + qm;
+            const int qp = qstr ? qp0 + (qm - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
+            const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
+            s[v] = ok ? s[v] : NEG_INF;
+          }
+        }
         // P and dS per half u of this lane's 16 rows (rows hr0 + 16u + 8hf + i2),
         // packed to bf16 as they are made; lse (to base 2) and delta of the
-        // 8 rows come as two 16-byte reads each.  Fully visible blocks take a
-        // copy of the loop without the visibility test.
+        // 8 rows come as two 16-byte reads each.  A row without any visible
+        // key has lse = -inf; its exponent offset is clamped to the largest
+        // finite float, so that exp2(-inf + offset) = 0 there too.
+        f32x4 la[2], lb[2], da[2], db[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int qb = hr0 + 16 * u + 8 * hf;
-          const f32x4 la = *reinterpret_cast<const f32x4*>(sLse + qb);
-          const f32x4 lb = *reinterpret_cast<const f32x4*>(sLse + qb + 4);
-          const f32x4 da = *reinterpret_cast<const f32x4*>(sDel + qb);
-          const f32x4 db = *reinterpret_cast<const f32x4*>(sDel + qb + 4);
-          bf16x8 pb, sb;
-          if (wave_full) {
+          la[u] = *reinterpret_cast<const f32x4*>(sLse + qb);
+          lb[u] = *reinterpret_cast<const f32x4*>(sLse + qb + 4);
+          da[u] = *reinterpret_cast<const f32x4*>(sDel + qb);
+          db[u] = *reinterpret_cast<const f32x4*>(sDel + qb + 4);
+        }
+        bf16x8 pb[2], sb[2];
+        auto softmax_row = [&](int u, int i2) {
+          const int v = 8 * u + i2;
+          const float lse = i2 < 4 ? la[u][i2] : lb[u][i2 - 4];
+          const float del = i2 < 4 ? da[u][i2] : db[u][i2 - 4];
+          const float e = ex2(__builtin_fmaf(s[v], sl2, fminf(-lse * LOG2E, FLT_MAX_F)));
+          pb[u][i2] = (__bf16)e;
+          sb[u][i2] = (__bf16)(e * (dp[v] - del));
+        };
 #pragma unroll
-            for (int i2 = 0; i2 < 8; ++i2) {
-              const int v = 8 * u + i2;
-              const float lse = i2 < 4 ? la[i2] : lb[i2 - 4];
-              const float del = i2 < 4 ? da[i2] : db[i2 - 4];
-              const float e = ex2(__builtin_fmaf(s[v], sl2, -lse * LOG2E));
-              pb[i2] = (__bf16)e;
-              sb[i2] = (__bf16)(e * (dp[v] - del));
-            }
-          } else {
-            int hq = 8 * hf;
-            asm volatile("" : "+v"(hq));  // keeps the 16 row indices from being precomputed
+        for (int i2 = 0; i2 < 8; ++i2) softmax_row(0, i2);
+        pend[0] = sb[0];
+        // The products of half 0, pair by pair, each pair with the operand
+        // reads of the next pair and two rows of half 1's softmax; then the
+        // products of half 1.  The scheduling fences keep that order.
+        bf16x8 op_do = tr_op(sDO, 0, 0), op_q = tr_op(sQ, 0, 0);
 #pragma unroll
-            for (int i2 = 0; i2 < 8; ++i2) {
-              const int v = 8 * u + i2;
-              const float lse = i2 < 4 ? la[i2] : lb[i2 - 4];
-              const float del = i2 < 4 ? da[i2] : db[i2 - 4];
-              const int qm = hr0 + 16 * u + hq + i2;
-              const int r = qt * BQB + qm;
-              const int qp = qstr ? qp0 + (qm - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
-              const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
-              const float e = ok ? ex2(__builtin_fmaf(s[v], sl2, -lse * LOG2E)) : 0.f;
-              pb[i2] = (__bf16)e;
-              sb[i2] = (__bf16)(e * (dp[v] - del));
-            }
+        for (int k = 0; k < 2 * NDB; ++k) {
+          const int u = k / NDB, d = k % NDB;
+          bf16x8 nx_do = op_do, nx_q = op_q;
+          if (k + 1 < 2 * NDB) {
+            nx_do = tr_op(sDO, (k + 1) / NDB, (k + 1) % NDB);
+            nx_q = tr_op(sQ, (k + 1) / NDB, (k + 1) % NDB);
           }
-          pend[u] = sb;
+          dv[d] = mfma_bf16(op_do, pb[u], dv[d]);
+          dk[d] = mfma_bf16(op_q, sb[u], dk[d]);
+          if (u == 0) {
 #pragma unroll
-          for (int d = 0; d < NDB; ++d) {
-            dv[d] = mfma_bf16(tr_op(sDO, u, d), pb, dv[d]);
-            dk[d] = mfma_bf16(tr_op(sQ, u, d), sb, dk[d]);
+            for (int i = 0; i < 8 / NDB; ++i) softmax_row(1, (8 / NDB) * d + i);
+            if (d == NDB - 1) pend[1] = sb[1];
           }
-          // the transposed reads of a pair of products are issued one pair ahead
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-          for (int d = 0; d < NDB - 2; ++d) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          op_do = nx_do;
+          op_q = nx_q;
         }
       }
       // This tile's block of dS^T is stored with the next tile; blocks that
