@@ -2,25 +2,28 @@
 //
 // Forward block step ("Ring Flash Attention" README: each block returns its
 // output and softmax_lse; guijiagi.com Ring Attention article, online-softmax
-// section: running max / running sum rescaling).  One workgroup = 4 waves =
-// 128 query rows; each wave owns 32 query rows and walks the K/V block in
-// tiles of 64 keys staged through LDS.
+// section: running max / running sum rescaling) and its backward (textbook
+// softmax-attention gradient with P recomputed from the final lse).
 //
-// MFMA orientation.  The wave computes S^T = K * Q^T (M = 32 keys, N = 32
-// queries) so that in the MFMA result layout every lane holds ONE query and
-// 16 keys: the row max / row sum of the online softmax are per-lane
+// MFMA orientation.  A forward wave computes S^T = K * Q^T (M = 32 keys, N =
+// 32 queries) so that in the MFMA result layout every lane holds ONE query
+// and 16 keys: the row max / row sum of the online softmax are per-lane
 // reductions plus one exchange between the two 32-lane halves.  The A-operand
 // rows (keys) are permuted (bits 2 and 3 of the row index swapped) so that the
 // result registers of each half are 8 consecutive keys, which is exactly the
 // B-operand layout of the next product O^T += V^T * P^T (K-dim = keys).
-// V is therefore staged TRANSPOSED in LDS ([d][key], 16-byte chunks XOR
-// swizzled), so the A operand V^T is one 16-byte LDS read per lane.
 //
-// Backward block step (textbook softmax-attention gradient with P recomputed
-// from the final lse).  One workgroup = 4 waves = 128 keys (32 per wave); it
-// walks the query rows in tiles of 64 staged in LDS (natural and transposed),
-// keeps dK^T and dV^T in registers and adds dQ with fp32 atomics after a
-// round trip of dS through LDS.
+// Two families of kernels:
+//  * bf16 inputs (the measured path): fwd_kernel_bf16 (4 waves, 128 query
+//    rows, 64-key tiles), bwd_dkdv_kernel (8 waves, 128 keys, 64-row query
+//    tiles; stores dS), bwd_dq_ds_kernel (dQ = dS K from the stored dS) and
+//    bwd_dq_kernel (dQ with S and dP recomputed, when there is no room for
+//    dS).  Tiles are copied by buffer->LDS DMA in natural [row][d] layout with
+//    XOR-swizzled 16-byte chunks; transposed operands come from
+//    ds_read_b64_tr_b16.
+//  * fp32 inputs (the tight-tolerance parity path): fwd_kernel<D, false> and
+//    the fused bwd_kernel<D, false>, with register-staged tiles (V stored
+//    transposed in LDS), fp32 MFMA, and dQ added with fp32 atomics.
 //
 // Masks are evaluated on global token positions (see ra.h): per query row a
 // visible key interval [lo, hi] follows from the causal flag and cu_seqlens;
@@ -1363,9 +1366,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
 //  * dQ kernel: a workgroup owns 128 query rows (32 per wave) and walks the
 //    key tiles they can see: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T,
 //    dQ^T += K^T dS^T.  K/V tiles are DMA'd one tile ahead.
-// Both recompute P from the final lse; S and dP are computed twice (7 matrix
-// products per pair instead of 5), bought back by the absence of atomics and
-// by each kernel's smaller register and LDS footprint.
+// Both recompute P from the final lse.  With a workspace large enough for
+// the bf16 dS of one ring step, the dK/dV kernel also stores dS and dQ = dS K
+// is one product (bwd_dq_ds_kernel): five matrix products per pair in all.
+// Otherwise the dQ kernel above recomputes S and dP (seven products per pair).
 // ============================================================================================
 
 constexpr int DQ_BK = 64;  // keys per dQ-kernel tile
