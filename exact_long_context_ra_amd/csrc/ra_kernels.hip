@@ -1290,10 +1290,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
       dma_tile_lean<D, FBK>(rk, kst, min(jt + 2, jt1) * FBK, dK, w, c16, lks);
       s_tile(sKn, nxt);
       p_v(cur, sV);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // K operands of the first two k-steps
 #pragma unroll
       for (int g = 0; g < 2 * (FBK / (1024 / (2 * D))) / 4; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one buffer->LDS copy
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // operands two k-steps ahead
       }
       wait_vmem();
       if (jt + 1 <= jt1) mask_max(jt + 1, nxt);
