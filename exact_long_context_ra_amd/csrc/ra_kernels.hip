@@ -48,7 +48,6 @@ constexpr float POS_INF = __builtin_huge_valf();
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int INT_BIG = 0x7fffffff;
-constexpr float FLT_MAX_F = 3.40282347e+38f;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -1593,9 +1592,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        // lse (to base 2) and delta of this lane's 16 rows (rows hr0 + 16u +
+        // 8hf + i2 for half u) come as two 16-byte reads each.
+        f32x4 la[2], lb[2], da[2], db[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int qb = hr0 + 16 * u + 8 * hf;
+          la[u] = *reinterpret_cast<const f32x4*>(sLse + qb);
+          lb[u] = *reinterpret_cast<const f32x4*>(sLse + qb + 4);
+          da[u] = *reinterpret_cast<const f32x4*>(sDel + qb);
+          db[u] = *reinterpret_cast<const f32x4*>(sDel + qb + 4);
+        }
         // Blocks that are not fully visible set the scores of invisible
-        // (query, key) pairs to -inf first; what follows is the same
-        // straight-line code for every tile.
+        // (query, key) pairs to -inf first, and the lse of a row without any
+        // visible key (-inf) to +inf, so that exp2 gives 0 for all of them;
+        // what follows is the same straight-line code for every tile.
         if (!wave_full) {
           int hq = 8 * hf;
           asm volatile("" : "+v"(hq));  // keeps the 16 row indices from being precomputed
@@ -1607,27 +1618,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
             const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
             s[v] = ok ? s[v] : NEG_INF;
           }
-        }
-        // P and dS per half u of this lane's 16 rows (rows hr0 + 16u + 8hf + i2),
-        // packed to bf16 as they are made; lse (to base 2) and delta of the
-        // 8 rows come as two 16-byte reads each.  A row without any visible
-        // key has lse = -inf; its exponent offset is clamped to the largest
-        // finite float, so that exp2(-inf + offset) = 0 there too.
-        f32x4 la[2], lb[2], da[2], db[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int qb = hr0 + 16 * u + 8 * hf;
-          la[u] = *reinterpret_cast<const f32x4*>(sLse + qb);
-          lb[u] = *reinterpret_cast<const f32x4*>(sLse + qb + 4);
-          da[u] = *reinterpret_cast<const f32x4*>(sDel + qb);
-          db[u] = *reinterpret_cast<const f32x4*>(sDel + qb + 4);
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              la[u][i] = la[u][i] == NEG_INF ? POS_INF : la[u][i];
+              lb[u][i] = lb[u][i] == NEG_INF ? POS_INF : lb[u][i];
+            }
         }
+        // P and dS per half u of this lane's 16 rows, packed to bf16 as they
+        // are made.
         bf16x8 pb[2], sb[2];
         auto softmax_row = [&](int u, int i2) {
           const int v = 8 * u + i2;
           const float lse = i2 < 4 ? la[u][i2] : lb[u][i2 - 4];
           const float del = i2 < 4 ? da[u][i2] : db[u][i2 - 4];
-          const float e = ex2(__builtin_fmaf(s[v], sl2, fminf(-lse * LOG2E, FLT_MAX_F)));
+          const float e = ex2(__builtin_fmaf(s[v], sl2, -lse * LOG2E));
           pb[u][i2] = (__bf16)e;
           sb[u][i2] = (__bf16)(e * (dp[v] - del));
         };
