@@ -204,17 +204,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps; per-launch HIP events recorded by the
-    # library on the launch stream give each kernel's average duration.
+    # Timed region: exactly K steps, bracketed by synchronisations.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Kernel durations: K more steps with per-launch HIP events, which the
+    # library records on the launch stream around each of its kernels.  The
+    # event records leave a gap of about 10 us between launches, so these
+    # steps give the kernels' averages but not the step time above.
     with ra.kernel_timing(capacity=8192) as kt:
         torch.cuda.synchronize()
-        ev0.record(stream)
         for _ in range(args.steps):
             step()
-        ev1.record(stream)
         torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
 
     # Forward alone (second timed region, same inputs).
     torch.cuda.synchronize()
