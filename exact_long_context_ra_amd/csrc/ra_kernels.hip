@@ -1592,8 +1592,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        // lse (to base 2) and delta of this lane's 16 rows (rows hr0 + 16u +
-        // 8hf + i2 for half u) come as two 16-byte reads each.
+        // lse (natural log, taken to base 2 in the exponent) and delta of this
+        // lane's 16 rows (rows hr0 + 16u + 8hf + i2 for half u) come as two
+        // 16-byte reads each.
         f32x4 la[2], lb[2], da[2], db[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
