@@ -204,25 +204,28 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps, bracketed by synchronisations.
+    # Timed region: exactly K steps, bracketed by synchronisations; per-launch
+    # HIP events recorded by the library on the launch stream give each
+    # kernel's average duration.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with ra.kernel_timing(capacity=8192) as kt:
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # The per-launch event records leave about 10 us between launches; the
+    # same K steps without them, reported beside the headline for reference.
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-
-    # Kernel durations: K more steps with per-launch HIP events, which the
-    # library records on the launch stream around each of its kernels.  The
-    # event records leave a gap of about 10 us between launches, so these
-    # steps give the kernels' averages but not the step time above.
-    with ra.kernel_timing(capacity=8192) as kt:
-        torch.cuda.synchronize()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
+    ms_step_plain = ev0.elapsed_time(ev1) / args.steps
 
     # Forward alone (second timed region, same inputs).
     torch.cuda.synchronize()
@@ -290,6 +293,7 @@ def main():
         "fwd_tflops": round(fwd_tflops, 2),
         "pct_peak_fwd": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "ms_fwd": round(ms_fwd, 3),
+        "ms_per_step_without_launch_events": round(ms_step_plain, 3),
         "visible_pairs_per_head": total_pairs,
         "kernels": {n: {"launches": a["launches"], "avg_ms": round(a["ms"] / max(1, a["launches"]), 4),
                         **({"tflops": round(a["flops"] / (a["ms"] / 1e3) / 1e12, 1)} if a["flops"] and a["ms"] else {})}
