@@ -133,6 +133,39 @@ def test_ring_bwd(case, store_ds):
     check_grad(f64(dv_ring), oracle.to_ring(gv, layout, N, cu), bf, what="dv (all ranks)")
 
 
+@pytest.mark.parametrize("store_ds", [True, False], ids=["ds", "recompute"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
+def test_ring_bwd_noncausal(layout, store_ds):
+    """Without the causal mask every ring step is a fully visible block (the
+    layouts then only permute tokens): per-rank dQ and the summed dK/dV must
+    equal the gradients of full attention."""
+    import torch
+    ra = _ra()
+    S, N, H, D = 1024, 4, 2, 128
+    log(f"ring_bwd noncausal {layout} store_ds={store_ds}")
+    q, k, v, do = synth.qkv(S, H, D, _dtype("bf16"), seed=33, device="cpu", with_dout=True)
+    q, k, v, do = (x.to(dev()) for x in (q, k, v, do))
+    kr, idx = ring_from_global(k, layout, N, None)
+    vr, _ = ring_from_global(v, layout, N, None)
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
+    q64, k64, v64, do64 = f64(q), f64(k), f64(v), f64(do)
+    pos = np.arange(S)
+    ro, rl = oracle.attention(q64, k64, v64, pos, pos, False)
+    gq, gk, gv = oracle.attention_backward(q64, k64, v64, ro, rl, do64, pos, pos, False)
+    for r in range(N):
+        ql = q.index_select(1, idx[r]).contiguous()
+        dol = do.index_select(1, idx[r]).contiguous()
+        out, lse, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=False)
+        dq, _, _ = ra.ring_bwd(layout, N, r, ql, kr, vr, out, lse, dol, causal=False,
+                               dk_ring=dk_ring, dv_ring=dv_ring, store_ds=store_ds)
+        torch.cuda.synchronize()
+        opos = oracle.layout_positions(layout, S, N, r)
+        check_grad(f64(dq), gq[:, opos], True, what=f"dq r={r}")
+    check_grad(f64(dk_ring), oracle.to_ring(gk, layout, N), True, what="dk (all ranks)")
+    check_grad(f64(dv_ring), oracle.to_ring(gv, layout, N), True, what="dv (all ranks)")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_ring_per_sequence_on_user_stream(dt):
     """The per-sequence layouts run every sequence as a ring of its own: bf16

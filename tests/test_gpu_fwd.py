@@ -100,6 +100,8 @@ RING_CASES = [
     ("zigzag", 800, 4, 2, 64, "bf16", True, None, 1),         # chunks of 100: ragged tiles
     ("stripe", 1608, 8, 2, 64, "f32", True, None, 1),        # 201 rows per rank
     ("contiguous", 1600, 8, 2, 128, "bf16", False, None, 1),
+    ("zigzag", 1024, 4, 2, 128, "bf16", False, None, 2),      # non-causal: a permuted full attention
+    ("stripe", 1200, 4, 2, 64, "bf16", False, None, 1),
     ("contiguous", 1024, 1, 2, 128, "bf16", True, None, 1),   # N = 1: plain attention
     ("contiguous", 1536, 4, 2, 128, "bf16", True, "varlen", 1),
     ("zigzag", 1536, 4, 2, 128, "f32", True, "varlen", 1),
