@@ -1576,13 +1576,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
       }
       if (!wave_empty) {
         const int hr0 = qh * 32;
-        // S = Q K^T and dP = dO V^T, the two chains interleaved per k-step.
+        // S = Q K^T and dP = dO V^T, the two chains interleaved with S half
+        // of its k-steps ahead, so that S is complete while the last dP
+        // products run.
+        constexpr int LEAD = D / 32;
         f32x16 s = f32x16{}, dp = f32x16{};
         const int qrow = hr0 + row_perm(l32);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), row_operand<D>(sK, 32 * kg + l32, c, hf), s);
-          dp = mfma_bf16(row_operand<D>(sDO, qrow, c, hf), row_operand<D>(sV, 32 * kg + l32, c, hf), dp);
+        for (int c = 0; c < D / 16 + LEAD; ++c) {
+          if (c < D / 16)
+            s = mfma_bf16(row_operand<D>(sQ, qrow, c, hf), row_operand<D>(sK, 32 * kg + l32, c, hf), s);
+          if (c >= LEAD)
+            dp = mfma_bf16(row_operand<D>(sDO, qrow, c - LEAD, hf), row_operand<D>(sV, 32 * kg + l32, c - LEAD, hf),
+                           dp);
         }
         // The four operand reads of a k-step are issued one k-step ahead.
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
