@@ -52,6 +52,11 @@ _SIGS = {
     "ra_ring_bwd": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor, C.c_int64,
                     ra_tensor, C.c_void_p, ra_tensor, ra_tensor, ra_tensor, ra_tensor, C.c_int64,
                     C.c_void_p, C.c_size_t, C.c_void_p],
+    "ra_gathered_fwd": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor,
+                        ra_tensor, C.c_void_p, ra_tensor, C.c_void_p],
+    "ra_gathered_bwd": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor,
+                        ra_tensor, C.c_void_p, ra_tensor, ra_tensor, ra_tensor, ra_tensor,
+                        C.c_void_p, C.c_size_t, C.c_void_p],
     "ra_layout_positions": [C.c_int32, C.c_int64, C.c_int32, C.c_int32, P(C.c_int64)],
     "ra_layout_posmap": [C.c_int32, C.c_int64, C.c_int32, C.c_int32, P(ra_posmap)],
     "ra_layout_positions_cu": [C.c_int32, P(C.c_int32), C.c_int32, C.c_int32, C.c_int32, P(C.c_int64)],
@@ -78,6 +83,9 @@ def lib():
             fn.restype = C.c_int
         for name in ("ra_ring_workspace_bytes", "ra_ring_workspace_min_bytes"):
             getattr(L, name).argtypes = [P(ra_problem), C.c_int32, C.c_int32]
+            getattr(L, name).restype = C.c_size_t
+        for name in ("ra_gathered_workspace_bytes", "ra_gathered_workspace_min_bytes"):
+            getattr(L, name).argtypes = [P(ra_problem), C.c_int32, C.c_int32, C.c_int32]
             getattr(L, name).restype = C.c_size_t
         for name in ("ra_status_str", "ra_kernel_name"):
             getattr(L, name).restype = C.c_char_p

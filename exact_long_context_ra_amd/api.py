@@ -264,12 +264,75 @@ def ring_bwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, out, l
     return dq, dk_ring, dv_ring
 
 
-def cast_f32_to_bf16(x, out=None):
+# ---- gathered K/V share (llama3-style) -----------------------------------------------------
+
+def gathered_fwd(layout: str, world: int, rank: int, q_local, k_all, v_all, *, causal: bool = True,
+                 cu_seqlens=None, scale: Optional[float] = None, out=None, lse=None, want_lowp: bool = False,
+                 out_lowp=None):
+    """Rank ``rank``'s share against the whole gathered K/V ([b, S, h, d], global order), one
+    block step.  Returns (out fp32, lse fp32, out_lowp or None)."""
     torch = _torch()
-    if x.dtype != torch.float32 or not x.is_contiguous():
-        raise ValueError("expected a contiguous fp32 tensor")
+    b, L, h, d = q_local.shape
+    S = k_all.shape[1]
+    if S != L * world:
+        raise ValueError("k_all must hold world * local tokens")
+    if out is None:
+        out = torch.empty((b, L, h, d), device=q_local.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty((b, h, L), device=q_local.device, dtype=torch.float32)
+    if want_lowp and out_lowp is None:
+        out_lowp = torch.empty((b, L, h, d), device=q_local.device, dtype=q_local.dtype)
+    cu = _Cu(cu_seqlens, q_local.device)
+    p = _problem(q_local, h, d, S, causal, scale, cu)
+    check(lib().ra_gathered_fwd(C.byref(p), _layout_id(layout), world, rank, _t4(q_local), _t4(k_all), _t4(v_all),
+                                _t4(out), lse.data_ptr(), _t4(out_lowp), _stream()))
+    return out, lse, out_lowp
+
+
+def gathered_workspace_bytes(layout: str, world: int, rank: int, q_local, causal: bool = True,
+                             minimal: bool = False, cu_seqlens=None) -> int:
+    b, L, h, d = q_local.shape
+    p = _problem(q_local, h, d, L * world, causal, None, _Cu(cu_seqlens, q_local.device))
+    fn = lib().ra_gathered_workspace_min_bytes if minimal else lib().ra_gathered_workspace_bytes
+    return int(fn(C.byref(p), _layout_id(layout), world, rank))
+
+
+def gathered_bwd(layout: str, world: int, rank: int, q_local, k_all, v_all, out, lse, dout, *,
+                 causal: bool = True, cu_seqlens=None, scale: Optional[float] = None, dq=None, dk_all=None,
+                 dv_all=None, workspace=None, store_ds: bool = True):
+    """Backward of gathered_fwd's share: dq overwritten, dk_all/dv_all (fp32, global order)
+    accumulated (allocated zeroed when not given).  Returns (dq, dk_all, dv_all)."""
+    torch = _torch()
+    b, L, h, d = q_local.shape
+    S = k_all.shape[1]
+    dev = q_local.device
+    if dq is None:
+        dq = torch.empty((b, L, h, d), device=dev, dtype=torch.float32)
+    if dk_all is None:
+        dk_all = torch.zeros((b, S, h, d), device=dev, dtype=torch.float32)
+    if dv_all is None:
+        dv_all = torch.zeros((b, S, h, d), device=dev, dtype=torch.float32)
+    cu = _Cu(cu_seqlens, dev)
+    p = _problem(q_local, h, d, S, causal, scale, cu)
+    fn = lib().ra_gathered_workspace_bytes if store_ds else lib().ra_gathered_workspace_min_bytes
+    need = int(fn(C.byref(p), _layout_id(layout), world, rank))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), device=dev, dtype=torch.uint8)
+    check(lib().ra_gathered_bwd(C.byref(p), _layout_id(layout), world, rank, _t4(q_local), _t4(k_all), _t4(v_all),
+                                _t4(out), lse.data_ptr(), _t4(dout), _t4(dq), _t4(dk_all), _t4(dv_all),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return dq, dk_all, dv_all
+
+
+def cast_f32_to_bf16(x, out=None):
+    """bf16 copy of a contiguous fp32 device tensor (round to nearest, ties to even)."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("expected a contiguous fp32 device tensor")
     if out is None:
         out = torch.empty(x.shape, device=x.device, dtype=torch.bfloat16)
+    elif out.dtype != torch.bfloat16 or not out.is_contiguous() or out.numel() != x.numel():
+        raise ValueError("out must be a contiguous bf16 tensor of the same size")
     check(lib().ra_cast_f32_to_bf16(x.data_ptr(), out.data_ptr(), x.numel(), _stream()))
     return out
 

@@ -311,7 +311,6 @@ const char* ra_kernel_name(int32_t id) {
     case K_BWD_DQ_DS: return "block_bwd_dq_ds";
     case K_MERGE: return "lse_merge";
     case K_PREP: return "bwd_preprocess";
-    case K_FILL: return "fill";
     case K_CAST: return "cast_bf16";
     case K_ZERO: return "zero";
   }
@@ -1065,6 +1064,161 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     st = run_piece(pieces[i], pool->st[where[i]], nullptr);
   const ra_status sj = join_streams(pool, ns, s);
   return st != RA_OK ? st : sj;
+}
+
+
+// ---- gathered K/V share (llama3-style context parallelism) --------------------------------
+//
+// Every rank holds the whole K/V in global token order (all-gathered) and
+// attends its local queries to it as ONE block step (SourcePulse page on
+// ring-flash-attention, "How It Works" and "Highlighted Details").  Only the
+// key range the rank's queries can see is handed to the kernels: under the
+// causal mask nothing past the last query position, and with cu_seqlens
+// nothing before the start of the first query's sequence (or past the end of
+// the last one's).
+
+static ra_status gathered_common(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                                 ra_posmap* qmap, int64_t* L, int64_t* k_lo, int64_t* nk) {
+  ra_status st = check_problem(prob);
+  if (st != RA_OK) return st;
+  RA_CHECK(layout == RA_LAYOUT_CONTIGUOUS || layout == RA_LAYOUT_ZIGZAG || layout == RA_LAYOUT_STRIPE,
+           RA_ERR_UNSUPPORTED, "gathered share: layout %d not supported (contiguous, zigzag or stripe)",
+           (int)layout);
+  if ((st = make_posmap(layout, prob->seq_len, world, rank, qmap)) != RA_OK) return st;
+  *L = prob->seq_len / world;
+  *k_lo = 0;
+  *nk = 0;
+  if (*L == 0) return RA_OK;
+  const int64_t qmin = pos_at(*qmap, 0), qmax = pos_at(*qmap, *L - 1);
+  int64_t lo = 0, hi = prob->causal ? qmax : prob->seq_len - 1;
+  if (prob->num_seqs > 0 && prob->cu_seqlens_host) {
+    const int32_t* cu = prob->cu_seqlens_host;
+    const int32_t* f = std::upper_bound(cu, cu + prob->num_seqs + 1, (int32_t)qmin);
+    lo = f[-1];  // start of the first query's sequence
+    if (!prob->causal) {
+      const int32_t* g = std::upper_bound(cu, cu + prob->num_seqs + 1, (int32_t)qmax);
+      hi = (g <= cu + prob->num_seqs ? *g : prob->seq_len) - 1;  // end of the last query's sequence
+    }
+  }
+  *k_lo = lo;
+  *nk = hi - lo + 1;
+  return RA_OK;
+}
+
+// dS^T bytes of a gathered share: b*h slices of round_up(nk, 128) keys x round_up(L, 128)
+// rows (bf16), 0 when not applicable (fp32, or a slice beyond 32-bit byte offsets).
+static size_t gathered_ds_bytes(const ra_problem* prob, int64_t L, int64_t nk) {
+  if (prob->dtype != RA_DTYPE_BF16 || L == 0 || nk <= 0) return 0;
+  const int64_t slice = (nk + BWD_BK - 1) / BWD_BK * BWD_BK * ds_ld_of(L) * 2;
+  if (slice >= ((int64_t)1 << 32)) return 0;
+  return (size_t)prob->batch * prob->heads * (size_t)slice;
+}
+
+size_t ra_gathered_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank) {
+  ra_posmap qm;
+  int64_t L = 0, k_lo = 0, nk = 0;
+  if (gathered_common(prob, layout, world, rank, &qm, &L, &k_lo, &nk) != RA_OK) return 0;
+  const size_t bytes = (size_t)prob->batch * prob->heads * L * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+size_t ra_gathered_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank) {
+  ra_posmap qm;
+  int64_t L = 0, k_lo = 0, nk = 0;
+  if (gathered_common(prob, layout, world, rank, &qm, &L, &k_lo, &nk) != RA_OK) return 0;
+  const size_t base = ((size_t)prob->batch * prob->heads * L * sizeof(float) + 255) & ~(size_t)255;
+  return base + gathered_ds_bytes(prob, L, nk);
+}
+
+ra_status ra_gathered_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                          ra_tensor k_all, ra_tensor v_all, ra_tensor out, float* lse, ra_tensor out_lowp,
+                          void* stream) {
+  ra_posmap qmap;
+  int64_t L = 0, k_lo = 0, nk = 0;
+  ra_status st = gathered_common(prob, layout, world, rank, &qmap, &L, &k_lo, &nk);
+  if (st != RA_OK) return st;
+  if (L == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("k_all", shift_rows(k_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
+  if ((st = check_tensor("v_all", shift_rows(v_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
+  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("out_lowp", out_lowp, esz, L, out_lowp.ptr != nullptr)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  const ra_posmap kmap{1, {ra_seg{k_lo, 1, nk}, ra_seg{0, 1, 0}}};
+  FwdArgs a{};
+  a.q = rd(q_local);
+  a.k = rd(shift_rows(k_all, k_lo, esz));
+  a.v = rd(shift_rows(v_all, k_lo, esz));
+  a.out = wr(out);
+  a.lse = lse;
+  a.lse_sh = L;
+  a.out_lowp = wr(out_lowp);
+  a.batch = prob->batch;
+  a.heads = prob->heads;
+  a.lq = (int32_t)L;
+  a.lk = (int32_t)nk;
+  a.qmap = to_dmap(qmap);
+  a.kmap = to_dmap(kmap);
+  a.mask = mask_of(prob);
+  a.scale_log2 = scale_of(prob) * 1.4426950408889634f;
+  a.mode = FWD_STORE;
+  a.n_qtiles = ceil_div(L, FWD_BQ);
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+  RA_HIP(timed(K_FWD, 0, s, [&] { return launch_fwd(a, prob->head_dim, bf16, s); }));
+  return RA_OK;
+}
+
+ra_status ra_gathered_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                          ra_tensor k_all, ra_tensor v_all, ra_tensor out, const float* lse, ra_tensor dout,
+                          ra_tensor dq, ra_tensor dk_all, ra_tensor dv_all, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  ra_posmap qmap;
+  int64_t L = 0, k_lo = 0, nk = 0;
+  ra_status st = gathered_common(prob, layout, world, rank, &qmap, &L, &k_lo, &nk);
+  if (st != RA_OK) return st;
+  if (L == 0) return RA_OK;
+  const size_t esz = elem_size(prob->dtype);
+  if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("k_all", shift_rows(k_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
+  if ((st = check_tensor("v_all", shift_rows(v_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
+  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dout", dout, esz, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dq", dq, 4, L, true)) != RA_OK) return st;
+  if ((st = check_tensor("dk_all", shift_rows(dk_all, k_lo, 4), 4, nk, true)) != RA_OK) return st;
+  if ((st = check_tensor("dv_all", shift_rows(dv_all, k_lo, 4), 4, nk, true)) != RA_OK) return st;
+  if ((st = check_ptr("lse", lse)) != RA_OK) return st;
+  const size_t need = ra_gathered_workspace_min_bytes(prob, layout, world, rank);
+  RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
+           "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  const size_t dsb = gathered_ds_bytes(prob, L, nk);
+  uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
+  float* delta = (float*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = prob->dtype == RA_DTYPE_BF16;
+
+  PrepArgs pa{};
+  pa.out = rd(out);
+  pa.dout = rd(dout);
+  pa.delta = delta;
+  pa.batch = prob->batch;
+  pa.heads = prob->heads;
+  pa.lq = (int32_t)L;
+  pa.dim = prob->head_dim;
+  RA_HIP(timed(K_PREP, -1, s, [&] { return launch_prep(pa, bf16, s); }));
+  Tensor4W dqw = wr(dq);
+  RA_HIP(timed(K_ZERO, -1, s, [&] {
+    return launch_zero(dqw, prob->batch, prob->heads, (int32_t)L, prob->head_dim, s);
+  }));
+  const ra_posmap kmap{1, {ra_seg{k_lo, 1, nk}, ra_seg{0, 1, 0}}};
+  BwdArgs a;
+  bwd_args(prob, q_local, L, qmap, rd(shift_rows(k_all, k_lo, esz)), rd(shift_rows(v_all, k_lo, esz)), nk, kmap,
+           dout, lse, delta, dqw, wr(shift_rows(dk_all, k_lo, 4)), wr(shift_rows(dv_all, k_lo, 4)), &a);
+  a.dsT = dsT;
+  a.ds_ld = ds_ld_of(L);
+  return launch_bwd_step(a, prob->head_dim, bf16, 0, s);
 }
 
 }  // extern "C"

@@ -104,19 +104,12 @@ struct PrepArgs {
   int32_t batch, heads, lq, dim;
 };
 
-struct FillArgs {
-  Tensor4W out;  // fp32, set to 0
-  float* lse;    // set to -inf
-  int32_t batch, heads, lq, dim;
-};
-
 // Kernel ids reported by the timing facility.
 enum KernelId : int32_t {
   K_FWD = 0,
   K_BWD = 1,  // bf16: dK/dV kernel; fp32: fused backward
   K_MERGE = 2,
   K_PREP = 3,
-  K_FILL = 4,
   K_CAST = 5,
   K_ZERO = 6,
   K_BWD_DQ = 7,     // bf16 dQ kernel (recomputes S and dP)
@@ -136,7 +129,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_fill(const FillArgs& a, hipStream_t s);
 hipError_t launch_cast(const float* src, void* dst, int64_t n, hipStream_t s);
 hipError_t launch_zero(const Tensor4W& t, int32_t batch, int32_t heads, int32_t rows, int32_t dim,
                        hipStream_t s);

@@ -2140,24 +2140,6 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   if (rid < rows && sub == 0) a.delta[((int64_t)b * a.heads + h) * a.lq + t] = acc;
 }
 
-// out rows = 0 (fp32, 4 at a time), lse = -inf.
-__global__ __launch_bounds__(NT) void fill_kernel(FillArgs a) {
-  const int64_t per_row = a.dim / 4;
-  const int64_t total = (int64_t)a.batch * a.lq * a.heads * per_row;
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (i < total) {
-    const int c = (int)(i % per_row);
-    int64_t rr = i / per_row;
-    const int h = (int)(rr % a.heads);
-    rr /= a.heads;
-    const int t = (int)(rr % a.lq);
-    const int b = (int)(rr / a.lq);
-    float* o = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)t * a.out.st + h * a.out.sh + 4 * c;
-    *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  if (i < (int64_t)a.batch * a.heads * a.lq) a.lse[i] = NEG_INF;
-}
-
 __global__ __launch_bounds__(NT) void zero_kernel(Tensor4W t, int32_t batch, int32_t heads, int32_t rows, int32_t dim) {
   const int64_t per_row = dim / 4;
   const int64_t total = (int64_t)batch * rows * heads * per_row;
@@ -2173,9 +2155,34 @@ __global__ __launch_bounds__(NT) void zero_kernel(Tensor4W t, int32_t batch, int
   *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-__global__ __launch_bounds__(NT) void cast_kernel(const float* src, uint16_t* dst, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (i < n) dst[i] = __builtin_bit_cast(uint16_t, (__bf16)src[i]);
+// fp32 -> bf16, round to nearest, ties to even, on the bit pattern (so the
+// result does not depend on the wave's float mode: subnormals round like any
+// other value); a NaN stays a NaN with its sign and top payload bits, quieted.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eight elements per thread: two 16-byte loads and one 16-byte store when
+// both pointers are 16-byte aligned, element by element otherwise (and in the
+// last, partial group).
+__global__ __launch_bounds__(NT) void cast_kernel(const float* src, uint16_t* dst, int64_t n, int vec) {
+  const int64_t i = ((int64_t)blockIdx.x * NT + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (vec && i + 8 <= n) {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + i);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + i + 4);
+    u32x4 w;
+    w[0] = bf16_bits_rne(x0[0]) | (bf16_bits_rne(x0[1]) << 16);
+    w[1] = bf16_bits_rne(x0[2]) | (bf16_bits_rne(x0[3]) << 16);
+    w[2] = bf16_bits_rne(x1[0]) | (bf16_bits_rne(x1[1]) << 16);
+    w[3] = bf16_bits_rne(x1[2]) | (bf16_bits_rne(x1[3]) << 16);
+    *reinterpret_cast<u32x4*>(dst + i) = w;
+    return;
+  }
+  const int64_t e = i + 8 < n ? i + 8 : n;
+  for (int64_t j = i; j < e; ++j) dst[j] = (uint16_t)bf16_bits_rne(src[j]);
 }
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
@@ -2273,18 +2280,11 @@ hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill(const FillArgs& a, hipStream_t s) {
-  const int64_t n_out = (int64_t)a.batch * a.lq * a.heads * (a.dim / 4);
-  const int64_t n_lse = (int64_t)a.batch * a.heads * a.lq;
-  const int64_t n = n_out > n_lse ? n_out : n_lse;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(n)), dim3(NT), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_cast(const float* src, void* dst, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(cast_kernel, dim3(blocks_for(n)), dim3(NT), 0, s, src, reinterpret_cast<uint16_t*>(dst), n);
+  const int vec = (((uintptr_t)src | (uintptr_t)dst) & 15) == 0 ? 1 : 0;
+  hipLaunchKernelGGL(cast_kernel, dim3(blocks_for((n + 7) / 8)), dim3(NT), 0, s, src,
+                     reinterpret_cast<uint16_t*>(dst), n, vec);
   return hipGetLastError();
 }
 

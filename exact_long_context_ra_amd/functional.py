@@ -15,8 +15,16 @@ backward recomputes P from the saved lse).
 
 The llama3-style context-parallel share (SourcePulse summary of the
 reference, "How It Works" / "Highlighted Details": gather all K/V, then a
-rank attends its local queries against them) is `gathered_share_attn`: one
-block step over the whole gathered K/V with the rank's global positions.
+rank attends its local queries against them; recommended there for varlen)
+is `gathered_share_attn` for one rank and `gathered_attn_func` /
+`llama3_attn_varlen_func` for every rank of a virtual context-parallel group:
+one block step per rank over the whole gathered K/V (ra_gathered_fwd /
+ra_gathered_bwd), differentiable.
+
+Low-precision results (the bf16 output of a bf16 call, and the bf16 gradients)
+come from the library as well: the forward kernel writes the bf16 copy of the
+output with the last ring step, and the gradients are cast by
+ra_cast_f32_to_bf16 (round to nearest, ties to even).
 """
 from __future__ import annotations
 
@@ -28,6 +36,16 @@ from . import api
 def _torch():
     import torch
     return torch
+
+
+def _lowp(x32, dtype):
+    """``x32`` (fp32) in ``dtype``: itself for fp32, the library's RNE copy for bf16."""
+    torch = _torch()
+    if dtype == torch.float32:
+        return x32
+    if dtype == torch.bfloat16:
+        return api.cast_f32_to_bf16(x32.contiguous())
+    raise TypeError(f"unsupported dtype {dtype} (bf16 or fp32)")
 
 
 def _positions(layout: str, S: int, world: int, device, cu_seqlens=None):
@@ -49,13 +67,14 @@ class _VirtualRing:
         out = torch.empty((b, S, h, d), device=q.device, dtype=q.dtype)
         lse = torch.empty((b, h, S), device=q.device, dtype=torch.float32)
         outs, lses = [], []
+        lowp = q.dtype != torch.float32
         for r in range(world):
             ql = q.index_select(1, idx[r]).contiguous()
-            o32, l, _ = api.ring_fwd(layout, world, r, ql, k_ring, v_ring, causal=causal, cu_seqlens=cu_seqlens,
-                                     scale=scale)
+            o32, l, olp = api.ring_fwd(layout, world, r, ql, k_ring, v_ring, causal=causal, cu_seqlens=cu_seqlens,
+                                       scale=scale, want_lowp=lowp)
             outs.append(o32)
             lses.append(l)
-            out.index_copy_(1, idx[r], o32.to(q.dtype))
+            out.index_copy_(1, idx[r], olp if lowp else o32)
             lse.index_copy_(2, idx[r], l)
         return out, lse, (idx, k_ring, v_ring, outs, lses)
 
@@ -104,7 +123,7 @@ def _make_function():
                                                ctx.saved)
             ctx.saved = None
             qd, kd, vd = ctx.dtypes
-            return dq.to(qd), dk.to(kd), dv.to(vd), None, None, None, None, None
+            return _lowp(dq, qd), _lowp(dk, kd), _lowp(dv, vd), None, None, None, None, None
 
     return RingAttentionFn
 
@@ -154,14 +173,131 @@ def ring_attn_qkvpacked_func(qkv, **kw):
     return ring_attn_func(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], **kw)
 
 
+def _make_gathered_function():
+    torch = _torch()
+
+    class GatheredShareFn(torch.autograd.Function):
+        """One rank's share against the whole gathered K/V (global order)."""
+
+        @staticmethod
+        def forward(ctx, q_local, k_all, v_all, layout, world, rank, causal, cu_seqlens, scale):
+            q_local, k_all, v_all = q_local.detach(), k_all.detach(), v_all.detach()
+            lowp = q_local.dtype != torch.float32
+            o32, lse, olp = api.gathered_fwd(layout, world, rank, q_local, k_all, v_all, causal=causal,
+                                             cu_seqlens=cu_seqlens, scale=scale, want_lowp=lowp)
+            ctx.save_for_backward(q_local, k_all, v_all, o32, lse)
+            ctx.args = (layout, world, rank, causal, cu_seqlens, scale)
+            ctx.mark_non_differentiable(lse)
+            return (olp if lowp else o32), lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            q_local, k_all, v_all, o32, lse = ctx.saved_tensors
+            layout, world, rank, causal, cu_seqlens, scale = ctx.args
+            dq, dk, dv = api.gathered_bwd(layout, world, rank, q_local, k_all, v_all, o32, lse,
+                                          dout.contiguous().to(q_local.dtype), causal=causal,
+                                          cu_seqlens=cu_seqlens, scale=scale)
+            return (_lowp(dq, q_local.dtype), _lowp(dk, k_all.dtype), _lowp(dv, v_all.dtype),
+                    None, None, None, None, None, None)
+
+    return GatheredShareFn
+
+
+_GFN = None
+
+
 def gathered_share_attn(q_local, k_all, v_all, *, layout: str = "contiguous", world: int = 8, rank: int = 0,
                         causal: bool = True, cu_seqlens=None, softmax_scale: Optional[float] = None):
     """One rank's share when all K/V have been gathered (llama3-style context
-    parallelism): q_local [b, S/N, h, d] of `rank` in `layout` attends to the
-    whole k_all/v_all [b, S, h, d] in global order, as a single block step.
-    Returns (out fp32, lse fp32)."""
-    S = k_all.shape[1]
-    qm = api.layout_posmap(layout, S, world, rank)
-    km = api.posmap([(0, 1, S)])
-    return api.block_attn_fwd(q_local, k_all, v_all, qm, km, seq_len=S, causal=causal, cu_seqlens=cu_seqlens,
-                              scale=softmax_scale)
+    parallelism): q_local [b, S/N, h, d] of `rank` in `layout` (contiguous, zigzag
+    or stripe) attends to the whole k_all/v_all [b, S, h, d] in global order, as a
+    single block step.  Returns (out in q_local's dtype, lse fp32 [b, h, S/N]);
+    differentiable with respect to q_local, k_all and v_all."""
+    global _GFN
+    if _GFN is None:
+        _GFN = _make_gathered_function()
+    return _GFN.apply(q_local, k_all, v_all, layout, world, rank, causal, cu_seqlens, softmax_scale)
+
+
+def _make_gathered_group_function():
+    torch = _torch()
+
+    class GatheredGroupFn(torch.autograd.Function):
+        """Every rank of an N-rank llama3-style group, gradients summed over the
+        ranks in fp32 before the one cast to the input dtype."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, layout, world, causal, cu_seqlens, scale):
+            q, k, v = q.detach(), k.detach(), v.detach()
+            b, S, h, d = q.shape
+            idx = _positions(layout, S, world, q.device)
+            lowp = q.dtype != torch.float32
+            out = torch.empty((b, S, h, d), device=q.device, dtype=q.dtype)
+            lse = torch.empty((b, h, S), device=q.device, dtype=torch.float32)
+            saved = []
+            for r in range(world):
+                ql = q.index_select(1, idx[r]).contiguous()
+                o32, l, olp = api.gathered_fwd(layout, world, r, ql, k, v, causal=causal, cu_seqlens=cu_seqlens,
+                                               scale=scale, want_lowp=lowp)
+                saved.append((o32, l))
+                out.index_copy_(1, idx[r], olp if lowp else o32)
+                lse.index_copy_(2, idx[r], l)
+            ctx.saved = (idx, saved)
+            ctx.args = (layout, world, causal, cu_seqlens, scale)
+            ctx.save_for_backward(q, k, v)
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            q, k, v = ctx.saved_tensors
+            idx, saved = ctx.saved
+            layout, world, causal, cu_seqlens, scale = ctx.args
+            b, S, h, d = q.shape
+            dq = torch.empty((b, S, h, d), device=q.device, dtype=torch.float32)
+            dk = torch.zeros((b, S, h, d), device=q.device, dtype=torch.float32)
+            dv = torch.zeros((b, S, h, d), device=q.device, dtype=torch.float32)
+            dout = dout.contiguous().to(q.dtype)
+            for r in range(world):
+                ql = q.index_select(1, idx[r]).contiguous()
+                dol = dout.index_select(1, idx[r]).contiguous()
+                o32, l = saved[r]
+                dqr, _, _ = api.gathered_bwd(layout, world, r, ql, k, v, o32, l, dol, causal=causal,
+                                             cu_seqlens=cu_seqlens, scale=scale, dk_all=dk, dv_all=dv)
+                dq.index_copy_(1, idx[r], dqr)
+            ctx.saved = None
+            return (_lowp(dq, q.dtype), _lowp(dk, k.dtype), _lowp(dv, v.dtype), None, None, None, None, None)
+
+    return GatheredGroupFn
+
+
+_GGFN = None
+
+
+def gathered_attn_func(q, k, v, *, layout: str = "contiguous", world: int = 8, causal: bool = True,
+                       cu_seqlens=None, softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """Exact attention of global [b, S, h, d] q/k/v as an N-rank llama3-style group:
+    every rank's local queries (in ``layout``) attend to the whole gathered K/V, and
+    the ranks' outputs go back to global order.  Differentiable; the K/V gradients are
+    the sum of every rank's contribution (what a reduce-scatter would return)."""
+    global _GGFN
+    if _GGFN is None:
+        _GGFN = _make_gathered_group_function()
+    out, lse = _GGFN.apply(q, k, v, layout, world, causal, cu_seqlens, softmax_scale)
+    return (out, lse) if return_lse else out
+
+
+def llama3_attn_varlen_func(q, k, v, cu_seqlens: Sequence[int], *, world: int = 8, causal: bool = True,
+                            softmax_scale: Optional[float] = None, return_lse: bool = False):
+    """Packed variable-length sequences ([1, T, h, d] or [T, h, d], ONE cu_seqlens)
+    through the llama3-style group: rank r holds the r-th contiguous slice of the
+    packed queries and attends to all gathered K/V of its sequences."""
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+    res = gathered_attn_func(q, k, v, layout="contiguous", world=world, causal=causal, cu_seqlens=cu_seqlens,
+                             softmax_scale=softmax_scale, return_lse=True)
+    out, lse = res
+    if squeeze:
+        out = out.squeeze(0)
+    return (out, lse) if return_lse else out

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 #define RA_MAX_TIMED_LAUNCHES 65536
 
 typedef enum {
@@ -144,10 +144,13 @@ ra_status ra_bwd_preprocess(const ra_problem* prob, int64_t lq, ra_tensor out, r
 
 /* Backward of one block step using the FINAL lse and delta of the rows:
  *   P = exp(scale*q.k - lse) on visible pairs, dV += P^T dO, dS = P*(dO.V^T - delta),
- *   dQ += scale*dS K, dK += scale*dS^T Q.
+ *   dQ += scale*dS K, dK += scale*dS^T Q
+ * (the textbook gradient of softmax attention; the pages give no backward).
  * dq_acc (fp32 [b, lq, h, d]), dk_acc and dv_acc (fp32 [b, lk, h, d]) are ACCUMULATED
- * (+=).  dq_acc is updated with fp32 atomics; concurrent calls on other streams that
- * touch the same dk_acc/dv_acc rows race. */
+ * (+=).  For bf16 all three are updated by plain read-modify-write (no atomics);
+ * for fp32 dq_acc is updated with fp32 atomics and dk_acc/dv_acc by plain
+ * read-modify-write.  Calls that may run concurrently (other streams) must not
+ * share any rows of these buffers. */
 ra_status ra_block_attn_bwd(const ra_problem* prob,
                             ra_tensor q, int64_t lq, ra_posmap qmap,
                             ra_tensor k, ra_tensor v, int64_t lk, ra_posmap kmap,
@@ -186,8 +189,8 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
  *  [b, S/N, h, d]; ACCUMULATED (+=) with this rank's contribution, so that running
  *  every rank into the same buffers yields the full gradients.
  *  workspace: device memory, 16-byte aligned, of at least ra_ring_workspace_min_bytes()
- *  bytes.  It holds delta = rowsum(dO * O) (the preprocessing step of the backward in
- *  "Ring Flash Attention", zhuzilin/ring-flash-attention README) and, for bf16 when it
+ *  bytes.  It holds delta = rowsum(dO * O) (the row term of the textbook softmax-attention
+ *  gradient; the pages give no backward) and, for bf16 when it
  *  reaches ra_ring_workspace_bytes(), the bf16 dS^T of the current step: the dK/dV
  *  kernel then stores dS and dQ = dS K is one product per pair instead of a recompute
  *  of S, P and dP.  With less than that, dQ is computed by the recompute kernel.
@@ -209,6 +212,43 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t
 /* Smallest workspace ra_ring_bwd accepts (delta only; 0 on invalid input). */
 size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world);
 
+/* ---- gathered K/V share (llama3-style context parallelism) ------------------------------- */
+
+/* Rank `rank`'s share when every rank holds the whole K/V (all-gathered) instead of
+ * receiving it block by block: its local queries attend to all keys in ONE block step
+ * (SourcePulse page on ring-flash-attention, "How It Works" and "Highlighted Details":
+ * the llama3 variant gathers K/V first; the page recommends it for varlen use).
+ *  layout: CONTIGUOUS, ZIGZAG or STRIPE (which local queries the rank holds; the
+ *          per-sequence layouts are RA_ERR_UNSUPPORTED here).
+ *  q_local: [b, S/N, h, d] in prob->dtype, local tokens in layout order.
+ *  k_all, v_all: [b, S, h, d] in GLOBAL token order.  Only the keys the rank's queries
+ *          can see are read: none past the last query position when causal, and with
+ *          cu_seqlens (and its host copy) none outside the sequences of the first and
+ *          last query.
+ *  out: fp32 [b, S/N, h, d] and lse: fp32 [b, h, S/N], OVERWRITTEN; out_lowp optional
+ *          (ptr NULL = none), the output in prob->dtype.
+ * Masks as everywhere: global positions, causal flag, cu_seqlens. */
+ra_status ra_gathered_fwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                          ra_tensor q_local, ra_tensor k_all, ra_tensor v_all,
+                          ra_tensor out, float* lse, ra_tensor out_lowp, void* stream);
+
+/* Backward of ra_gathered_fwd's share with its FINAL out/lse: dq fp32 [b, S/N, h, d]
+ * OVERWRITTEN; dk_all, dv_all fp32 [b, S, h, d] in global order ACCUMULATED (+=) over the
+ * keys the share sees, so that running every rank into the same buffers gives the full
+ * gradients (a reduce-scatter on a real ring).  Workspace as for ra_ring_bwd: at least
+ * ra_gathered_workspace_min_bytes() (delta; dQ then recomputes S and dP), or
+ * ra_gathered_workspace_bytes() for the stored-dS path (bf16 only, and only when one
+ * (batch, head) slice of dS^T stays below 4 GiB). */
+ra_status ra_gathered_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                          ra_tensor q_local, ra_tensor k_all, ra_tensor v_all,
+                          ra_tensor out, const float* lse, ra_tensor dout,
+                          ra_tensor dq, ra_tensor dk_all, ra_tensor dv_all,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of ra_gathered_bwd: its fastest path / the least it accepts (0 on invalid input). */
+size_t ra_gathered_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank);
+size_t ra_gathered_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank);
+
 /* ---- utilities ---------------------------------------------------------------------------- */
 
 /* host_pos_out[a] = global position of local token a of `rank` (S/N entries, host memory). */
@@ -226,7 +266,10 @@ ra_status ra_layout_positions_cu(ra_layout layout, const int32_t* cu_host, int32
 ra_status ra_layout_posmap(ra_layout layout, int64_t seq_len, int32_t world, int32_t rank,
                            ra_posmap* out);
 
-/* dst[i] = bf16 round-to-nearest-even of src[i], i < n (device pointers). */
+/* dst[i] = bf16 of src[i] for i < n (device pointers, no alignment needed; faster when
+ * both are 16-byte aligned): round to nearest, ties to even, subnormals included; a NaN
+ * stays a NaN (sign and top payload bits kept, quiet bit set).  The optional low-precision
+ * copies of out, dQ, dK and dV that the autograd forms return are made with it. */
 ra_status ra_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
 
 /* Kernel timing.  Between ra_timing_begin and ra_timing_end every kernel the library

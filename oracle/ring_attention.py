@@ -377,7 +377,3 @@ def to_ring(x_global, layout: str, world: int, cu_seqlens=None) -> np.ndarray:
     S = x_global.shape[1]
     return np.stack([x_global[:, layout_positions(layout, S, world, r, cu_seqlens)] for r in range(world)])
 
-
-def varlen_lengths_to_cu(lengths: Sequence[int]) -> np.ndarray:
-    """cu_seqlens (global offsets, length n+1) of packed sequences."""
-    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))])

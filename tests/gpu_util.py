@@ -106,3 +106,63 @@ def varlen_cu_many(S: int, unit: int, n: int = 21):
     rest = S - sum(lengths)
     assert rest > 0 and rest % unit == 0
     return synth.cu_seqlens(lengths + [rest])
+
+
+def oracle_rows_fwd_bwd(q, k, v, dout, qpos, kpos, causal, cu_seqlens=None, block=64, workers=None):
+    """The oracle's forward and backward for many query rows, run on row blocks
+    in a thread pool (numpy and BLAS release the GIL; BLAS is held to one thread
+    per block).  q/dout [b, Lq, h, d] (rows at positions qpos), k/v [b, Lk, h, d]
+    at SORTED positions kpos.  Each block is given only the keys it can see (a
+    contiguous range of kpos: none past its last row when causal, none before the
+    start of its first row's sequence with cu_seqlens); the keys left out are
+    masked for every row of the block, so the results are those of the whole key
+    set.  Returns out, lse, dq of the rows and the rows' contributions dk, dv to
+    every key (float64)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    assert np.all(np.diff(kpos) > 0), "kpos must be sorted"
+    B, Lq, H, Dh = q.shape
+    out = np.zeros((B, Lq, H, v.shape[3]))
+    lse = np.full((B, H, Lq), -np.inf)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    cu = None if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
+
+    def key_range(rows):
+        lo, hi = 0, kpos.size
+        pmin, pmax = int(qpos[rows].min()), int(qpos[rows].max())
+        if causal:
+            hi = int(np.searchsorted(kpos, pmax, side="right"))
+        if cu is not None:
+            s0 = int(cu[np.searchsorted(cu, pmin, side="right") - 1])
+            lo = int(np.searchsorted(kpos, s0, side="left"))
+            if not causal:
+                e1 = int(cu[np.searchsorted(cu, pmax, side="right")])
+                hi = int(np.searchsorted(kpos, e1, side="left"))
+        return lo, max(lo, hi)
+
+    def work(i0):
+        rows = np.arange(i0, min(Lq, i0 + block))
+        lo, hi = key_range(rows)
+        kb, vb, kp = k[:, lo:hi], v[:, lo:hi], kpos[lo:hi]
+        o, l = oracle.attention(q[:, rows], kb, vb, qpos[rows], kp, causal, cu_seqlens)
+        gq, gk, gv = oracle.attention_backward(q[:, rows], kb, vb, o, l, dout[:, rows], qpos[rows], kp, causal,
+                                               cu_seqlens)
+        return rows, lo, hi, o, l, gq, gk, gv
+
+    nw = workers or min(16, len(os.sched_getaffinity(0)))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=nw) as ex:
+        for rows, lo, hi, o, l, gq, gk, gv in ex.map(work, range(0, Lq, block)):
+            out[:, rows] = o
+            lse[:, :, rows] = l
+            dq[:, rows] = gq
+            dk[:, lo:hi] += gk
+            dv[:, lo:hi] += gv
+    return out, lse, dq, dk, dv

@@ -38,7 +38,7 @@ def test_header_symbols_exported(ra):
 
 def test_abi_version_and_strings(ra):
     lib = ra.lib()
-    assert lib.ra_abi_version() == 2
+    assert lib.ra_abi_version() == 3
     assert lib.ra_status_str(0) == b"RA_OK"
     assert lib.ra_status_str(4) == b"RA_ERR_WORKSPACE"
     assert lib.ra_kernel_name(0) == b"block_fwd"

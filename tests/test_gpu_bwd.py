@@ -213,3 +213,42 @@ def test_ring_per_sequence_on_user_stream(dt):
         assert torch.allclose(sums, ref_sums, rtol=1e-9 if dt == "bf16" else 1e-6, atol=0), \
             "results consumed on the user stream before the join completed"
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("store_ds", [True, False], ids=["ds", "recompute"])
+@pytest.mark.parametrize("dt,layout", [("bf16", "zigzag"), ("bf16", "stripe"), ("f32", "zigzag"),
+                                       ("f32", "contiguous")])
+def test_ring_softmax_scale(dt, layout, store_ds):
+    """An explicit softmax_scale through the ring forward and backward (every rank,
+    summed dK/dV) against the oracle with the same scale."""
+    import torch
+    ra = _ra()
+    if dt == "f32" and not store_ds:
+        pytest.skip("fp32 has one backward path")
+    scale, S, N, H, D = 0.05, 1024, 4, 2, 128
+    log(f"ring scale={scale} {layout} {dt} store_ds={store_ds}")
+    q, k, v, do = synth.qkv(S, H, D, _dtype(dt), seed=37, device="cpu", with_dout=True)
+    q, k, v, do = (x.to(dev()) for x in (q, k, v, do))
+    kr, idx = ring_from_global(k, layout, N)
+    vr, _ = ring_from_global(v, layout, N)
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
+    q64, k64, v64, do64 = f64(q), f64(k), f64(v), f64(do)
+    pos = np.arange(S)
+    ro, rl = oracle.attention(q64, k64, v64, pos, pos, True, scale=scale)
+    gq, gk, gv = oracle.attention_backward(q64, k64, v64, ro, rl, do64, pos, pos, True, scale=scale)
+    bf = dt == "bf16"
+    from gpu_util import check_lse, check_out
+    for r in range(N):
+        ql = q.index_select(1, idx[r]).contiguous()
+        dol = do.index_select(1, idx[r]).contiguous()
+        out, lse, _ = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True, scale=scale)
+        dq, _, _ = ra.ring_bwd(layout, N, r, ql, kr, vr, out, lse, dol, causal=True, scale=scale,
+                               dk_ring=dk_ring, dv_ring=dv_ring, store_ds=store_ds)
+        torch.cuda.synchronize()
+        opos = oracle.layout_positions(layout, S, N, r)
+        check_out(f64(out), ro[:, opos], bf, what=f"out r={r}")
+        check_lse(f64(lse), rl[:, :, opos], bf, what=f"lse r={r}")
+        check_grad(f64(dq), gq[:, opos], bf, what=f"dq r={r}")
+    check_grad(f64(dk_ring), oracle.to_ring(gk, layout, N), bf, what="dk (all ranks)")
+    check_grad(f64(dv_ring), oracle.to_ring(gv, layout, N), bf, what="dv (all ranks)")

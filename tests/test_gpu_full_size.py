@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_grad, check_lse, check_out, dev, f64, log, ring_from_global
+from gpu_util import check_grad, check_lse, check_out, dev, f64, log, oracle_rows_fwd_bwd, ring_from_global
 
 pytestmark = pytest.mark.gpu
 
@@ -146,6 +146,55 @@ def test_full_size_fwd_bwd(layout, S, rank):
     has = torch.ones(L, device=dev(), dtype=torch.float64)  # causal self-attention: every row sees itself
     _check_invariants(dk_ring, dv_ring, dol, has, f"{layout} r{rank}")
     _check_tail_dkdv(q, do, dk_ring, dv_ring, pos, idx, k64, v64, hsel, f"{layout} r{rank}")
+
+
+@pytest.mark.parametrize("layout,S,rank,heads", [("zigzag", 131072, 0, (0, 31)), ("stripe", 262144, 0, (0,))])
+def test_full_size_full_heads(layout, S, rank, heads):
+    """Element by element over WHOLE heads of the benchmark share: out, lse and dQ
+    of every query row, and this rank's dK/dV contributions to every key of all
+    N blocks, against the oracle (run on row blocks in threads), plus the sum
+    identities on every head."""
+    import time
+
+    import torch
+    ra = _ra()
+    N = 8
+    log(f"full-size full heads {layout} S={S} rank={rank} heads={heads}")
+    q, do, kr, vr, idx, k64, v64, hsel = _setup(layout, S, N, seed=0)
+    ql = q.index_select(1, idx[rank]).contiguous()
+    dol = do.index_select(1, idx[rank]).contiguous()
+    out, lse, _ = ra.ring_fwd(layout, N, rank, ql, kr, vr, causal=True)
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
+    dq, _, _ = ra.ring_bwd(layout, N, rank, ql, kr, vr, out, lse, dol, causal=True, dk_ring=dk_ring,
+                           dv_ring=dv_ring)
+    torch.cuda.synchronize()
+    L = S // N
+    _check_invariants(dk_ring, dv_ring, dol, torch.ones(L, device=dev(), dtype=torch.float64),
+                      f"{layout} r{rank}")
+    pos = oracle.layout_positions(layout, S, N, rank)
+    # rank-major ring rows -> global order (library positions, checked equal to the oracle's elsewhere)
+    perm = torch.cat(idx)
+    for h in heads:
+        j = HEADS.index(h)
+        t0 = time.perf_counter()
+        q64 = f64(ql[:, :, h:h + 1])
+        do64 = f64(dol[:, :, h:h + 1])
+        ro, rl, gq, gk, gv = oracle_rows_fwd_bwd(q64, k64[:, :, j:j + 1], v64[:, :, j:j + 1], do64, pos,
+                                                 np.arange(S), True)
+        log(f"{layout} r{rank} head {h}: oracle {time.perf_counter() - t0:.1f} s")
+        what = f"{layout} r{rank} head {h}"
+        check_out(f64(out[:, :, h:h + 1]), ro, True, what=f"{what} out")
+        check_lse(f64(lse[:, h:h + 1]), rl, True, what=f"{what} lse")
+        check_grad(f64(dq[:, :, h:h + 1]), gq, True, what=f"{what} dq")
+        dk_g = torch.empty((1, S, 1, D), device=dev(), dtype=torch.float32)
+        dv_g = torch.empty((1, S, 1, D), device=dev(), dtype=torch.float32)
+        dk_g[:, perm] = dk_ring[:, :, :, h:h + 1].permute(1, 0, 2, 3, 4).reshape(1, S, 1, D)
+        dv_g[:, perm] = dv_ring[:, :, :, h:h + 1].permute(1, 0, 2, 3, 4).reshape(1, S, 1, D)
+        ek = check_grad(f64(dk_g), gk, True, what=f"{what} dk")
+        ev = check_grad(f64(dv_g), gv, True, what=f"{what} dv")
+        log(f"{what}: dk max err {ek:.2e} (max|ref| {np.abs(gk).max():.2e}), dv {ev:.2e} "
+            f"(max|ref| {np.abs(gv).max():.2e})")
 
 
 def test_full_size_contiguous_all_ranks():

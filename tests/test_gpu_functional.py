@@ -100,19 +100,128 @@ def test_varlen_func_autograd(dt, layout):
     check_grad(f64(vg.grad)[None], gv, bf, what="dv")
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "stripe"])
-def test_gathered_share(layout):
-    """llama3-style share: a rank's queries against all gathered K/V in one block step."""
+@pytest.mark.parametrize("form", ["kvpacked", "qkvpacked"])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_packed_forms_gradients(form, dt):
+    """Gradients flow through the packed forms' strided views into the packed
+    tensor itself, and equal the oracle's gradients."""
     import torch
     ra = _ra()
-    log(f"gathered share {layout}")
+    log(f"packed gradients {form} {dt}")
+    S, H, D, N = 768, 2, 128, 4
+    qkv, do = synth.draw_normal([(1, S, 3, H, D), (1, S, H, D)], _dt(dt), seed=45, device="cpu")
+    qkv, do = qkv.to(dev()), do.to(dev())
+    if form == "qkvpacked":
+        x = qkv.clone().requires_grad_(True)
+        out = ra.ring_attn_qkvpacked_func(x, layout="stripe", world=N)
+        out.backward(do)
+        grads = [x.grad[:, :, i] for i in range(3)]
+    else:
+        qg = qkv[:, :, 0].clone().requires_grad_(True)
+        kv = qkv[:, :, 1:].clone().requires_grad_(True)
+        out = ra.ring_attn_kvpacked_func(qg, kv, layout="stripe", world=N)
+        out.backward(do)
+        grads = [qg.grad, kv.grad[:, :, 0], kv.grad[:, :, 1]]
+    torch.cuda.synchronize()
+    q64, k64, v64 = (f64(qkv[:, :, i]) for i in range(3))
+    pos = np.arange(S)
+    ro, rl = oracle.attention(q64, k64, v64, pos, pos, True)
+    gq, gk, gv = oracle.attention_backward(q64, k64, v64, ro, rl, f64(do), pos, pos, True)
+    bf = dt == "bf16"
+    check_out(f64(out), ro, bf)
+    for name, g, ref in zip(("dq", "dk", "dv"), grads, (gq, gk, gv)):
+        assert g.dtype == qkv.dtype
+        check_grad(f64(g), ref, bf, what=name)
+
+
+@pytest.mark.parametrize("store_ds", [True, False], ids=["ds", "recompute"])
+@pytest.mark.parametrize("layout,dt", [("contiguous", "bf16"), ("zigzag", "bf16"), ("stripe", "bf16"),
+                                       ("zigzag", "f32")])
+def test_gathered_share(layout, dt, store_ds):
+    """llama3-style share: a rank's queries against all gathered K/V in one block
+    step, forward and backward (this rank's contributions to dK/dV), through the
+    C ABI on both dQ paths."""
+    import torch
+    ra = _ra()
+    if dt == "f32" and not store_ds:
+        pytest.skip("fp32 has one backward path")
+    log(f"gathered share {layout} {dt} store_ds={store_ds}")
     S, H, D, N, r = 2048, 2, 128, 8, 3
-    q, k, v = synth.qkv(S, H, D, torch.bfloat16, seed=53, device="cpu")
-    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    q, k, v, do = synth.qkv(S, H, D, _dt(dt), seed=53, device="cpu", with_dout=True)
+    q, k, v, do = q.to(dev()), k.to(dev()), v.to(dev()), do.to(dev())
     idx = torch.from_numpy(ra.layout_positions(layout, S, N, r)).to(dev())
-    out, lse = ra.gathered_share_attn(q.index_select(1, idx).contiguous(), k, v, layout=layout, world=N, rank=r)
+    ql = q.index_select(1, idx).contiguous()
+    dol = do.index_select(1, idx).contiguous()
+    out, lse, lowp = ra.gathered_fwd(layout, N, r, ql, k, v, causal=True, want_lowp=True)
+    dq, dk, dv = ra.gathered_bwd(layout, N, r, ql, k, v, out, lse, dol, causal=True, store_ds=store_ds)
     torch.cuda.synchronize()
     pos = oracle.layout_positions(layout, S, N, r)
-    ro, rl = oracle.attention(f64(q)[:, pos], f64(k), f64(v), pos, np.arange(S), True)
-    check_out(f64(out), ro, True)
-    check_lse(f64(lse), rl, True)
+    q64 = f64(q)[:, pos]
+    ro, rl = oracle.attention(q64, f64(k), f64(v), pos, np.arange(S), True)
+    gq, gk, gv = oracle.attention_backward(q64, f64(k), f64(v), ro, rl, f64(do)[:, pos], pos, np.arange(S), True)
+    bf = dt == "bf16"
+    check_out(f64(out), ro, bf)
+    check_out(f64(lowp), ro, bf, what="out_lowp")
+    check_lse(f64(lse), rl, bf)
+    check_grad(f64(dq), gq, bf, what="dq")
+    check_grad(f64(dk), gk, bf, what="dk")
+    check_grad(f64(dv), gv, bf, what="dv")
+
+
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("f32", True), ("bf16", False)])
+def test_llama3_varlen_autograd(dt, causal):
+    """Packed sequences through the llama3-style group (every rank's contiguous
+    query slice against all gathered K/V of its sequences), with autograd, against
+    full varlen attention and its gradients."""
+    import torch
+    ra = _ra()
+    log(f"llama3 varlen {dt} causal={causal}")
+    N = 4
+    lengths = [7, 1, 300, 129, 1, 586, 1000]
+    T, H, D = sum(lengths) + (-sum(lengths)) % N, 2, 128
+    lengths[-1] += T - sum(lengths)
+    cu = synth.cu_seqlens(lengths)
+    q, k, v, do = synth.qkv(T, H, D, _dt(dt), seed=59, device="cpu", with_dout=True)
+    q, k, v, do = (x[0].to(dev()) for x in (q, k, v, do))  # [T, h, d]
+    qg, kg, vg = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out, lse = ra.llama3_attn_varlen_func(qg, kg, vg, cu, world=N, causal=causal, return_lse=True)
+    out.backward(do)
+    torch.cuda.synchronize()
+    pos = np.arange(T)
+    q64, k64, v64, do64 = (f64(x)[None] for x in (q, k, v, do))
+    ro, rl = oracle.attention(q64, k64, v64, pos, pos, causal, cu)
+    gq, gk, gv = oracle.attention_backward(q64, k64, v64, ro, rl, do64, pos, pos, causal, cu)
+    bf = dt == "bf16"
+    check_out(f64(out)[None], ro, bf)
+    check_lse(f64(lse), rl, bf)
+    check_grad(f64(qg.grad)[None], gq, bf, what="dq")
+    check_grad(f64(kg.grad)[None], gk, bf, what="dk")
+    check_grad(f64(vg.grad)[None], gv, bf, what="dv")
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "stripe"])
+def test_gathered_attn_func_matches_ring(layout):
+    """The llama3-style group and the virtual ring compute the same attention:
+    forward bit-for-bit is not expected (different key splits), parity with the
+    oracle for both, and the same gradients within the bf16 bound."""
+    import torch
+    ra = _ra()
+    log(f"gathered group vs ring {layout}")
+    S, H, D, N = 1024, 2, 64, 4
+    q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=61, device="cpu", with_dout=True)
+    q, k, v, do = (x.to(dev()) for x in (q, k, v, do))
+    res = []
+    for fn in (ra.gathered_attn_func, ra.ring_attn_func):
+        qg, kg, vg = (x.clone().requires_grad_(True) for x in (q, k, v))
+        out = fn(qg, kg, vg, layout=layout, world=N, causal=True)
+        out.backward(do)
+        res.append((out, qg.grad, kg.grad, vg.grad))
+    torch.cuda.synchronize()
+    pos = np.arange(S)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), pos, pos, True)
+    gq, gk, gv = oracle.attention_backward(f64(q), f64(k), f64(v), ro, rl, f64(do), pos, pos, True)
+    for out, dq, dk, dv in res:
+        check_out(f64(out), ro, True)
+        check_grad(f64(dq), gq, True, what="dq")
+        check_grad(f64(dk), gk, True, what="dk")
+        check_grad(f64(dv), gv, True, what="dv")

@@ -174,3 +174,25 @@ def test_ring_fwd_deterministic_and_teeth():
     dropped = oracle.ring_forward(layout, N, r, f64(ql), kr64, vr64, True, steps=[0, 1, 3])
     with pytest.raises(AssertionError):
         check_out(f64(o1), dropped[0], True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_block_fwd_softmax_scale(scale, dt):
+    """An explicit softmax_scale (not 1/sqrt(d)) reaches every score of the block step."""
+    import torch
+    ra = _ra()
+    log(f"block_fwd scale={scale} {dt}")
+    qsegs, ksegs, S = [(40, 1, 40), (400, 1, 40)], [(0, 1, 200), (300, 1, 140)], 440
+    qpos, kpos = _segs_positions(qsegs), _segs_positions(ksegs)
+    q, k, v = synth.draw_normal([(2, len(qpos), 2, 128), (2, len(kpos), 2, 128), (2, len(kpos), 2, 128)],
+                                _dtype(dt), seed=17, device="cpu")
+    q, k, v = q.to(dev()), k.to(dev()), v.to(dev())
+    out, lse = ra.block_attn_fwd(q, k, v, ra.posmap(qsegs), ra.posmap(ksegs), seq_len=S, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), qpos, kpos, True, scale=scale)
+    check_out(f64(out), ro, dt == "bf16")
+    check_lse(f64(lse), rl, dt == "bf16")
+    # the default scale gives a different result: the parameter is not ignored
+    rd_, _ = oracle.attention(f64(q), f64(k), f64(v), qpos, kpos, True)
+    assert np.abs(rd_ - ro).max() > 0.1
