@@ -6,7 +6,7 @@ this package only loads it and marshals torch tensors into its calls.
 from .api import (  # noqa: F401
     LAYOUTS, KernelTimes, block_attn_bwd, block_attn_fwd, bwd_preprocess, cast_f32_to_bf16,
     gathered_bwd, gathered_fwd, gathered_workspace_bytes, kernel_timing, layout_positions, layout_posmap,
-    lse_merge, posmap, ring_bwd, ring_fwd, ring_workspace_bytes,
+    lse_merge, noalloc_scratch_bytes, posmap, ring_bwd, ring_bwd_noalloc, ring_fwd, ring_workspace_bytes,
 )
 from ._lib import RAError, lib  # noqa: F401
 from .functional import (  # noqa: F401

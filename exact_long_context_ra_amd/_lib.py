@@ -52,6 +52,9 @@ _SIGS = {
     "ra_ring_bwd": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor, C.c_int64,
                     ra_tensor, C.c_void_p, ra_tensor, ra_tensor, ra_tensor, ra_tensor, C.c_int64,
                     C.c_void_p, C.c_size_t, C.c_void_p],
+    "ra_ring_bwd_noalloc": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor,
+                            C.c_int64, ra_tensor, C.c_void_p, ra_tensor, ra_tensor, ra_tensor, ra_tensor, C.c_int64,
+                            C.c_void_p],
     "ra_gathered_fwd": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor,
                         ra_tensor, C.c_void_p, ra_tensor, C.c_void_p],
     "ra_gathered_bwd": [P(ra_problem), C.c_int32, C.c_int32, C.c_int32, ra_tensor, ra_tensor, ra_tensor,
@@ -87,6 +90,8 @@ def lib():
         for name in ("ra_gathered_workspace_bytes", "ra_gathered_workspace_min_bytes"):
             getattr(L, name).argtypes = [P(ra_problem), C.c_int32, C.c_int32, C.c_int32]
             getattr(L, name).restype = C.c_size_t
+        L.ra_noalloc_scratch_bytes.argtypes = []
+        L.ra_noalloc_scratch_bytes.restype = C.c_size_t
         for name in ("ra_status_str", "ra_kernel_name"):
             getattr(L, name).restype = C.c_char_p
         L.ra_status_str.argtypes = [C.c_int]

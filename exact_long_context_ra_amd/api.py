@@ -264,6 +264,30 @@ def ring_bwd(layout: str, world: int, rank: int, q_local, k_ring, v_ring, out, l
     return dq, dk_ring, dv_ring
 
 
+def ring_bwd_noalloc(layout: str, world: int, rank: int, q_local, k_ring, v_ring, out, lse, dout, dq, dk_ring,
+                     dv_ring, *, causal: bool = True, cu_seqlens=None, scale: Optional[float] = None):
+    """ring_bwd for callers that cannot allocate: every buffer is the caller's, the
+    library's scratch is its fixed per-GPU array (noalloc_scratch_bytes()).  dq is
+    overwritten, dk_ring/dv_ring accumulated.  (cu_seqlens given as a device tensor is
+    copied to the host here; pass a host array to keep the call free of copies.)"""
+    b, L, h, d = q_local.shape
+    cu = _Cu(cu_seqlens, q_local.device)
+    p = _problem(q_local, h, d, L * world, causal, scale, cu)
+    kt, srank = _t5(k_ring)
+    vt, _ = _t5(v_ring)
+    dkt, sgrad = _t5(dk_ring)
+    dvt, sgrad_v = _t5(dv_ring)
+    if sgrad != sgrad_v:
+        raise ValueError("dk_ring and dv_ring must share the rank stride")
+    check(lib().ra_ring_bwd_noalloc(C.byref(p), _layout_id(layout), world, rank, _t4(q_local), kt, vt, srank,
+                                    _t4(out), lse.data_ptr(), _t4(dout), _t4(dq), dkt, dvt, sgrad, _stream()))
+    return dq, dk_ring, dv_ring
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().ra_noalloc_scratch_bytes())
+
+
 # ---- gathered K/V share (llama3-style) -----------------------------------------------------
 
 def gathered_fwd(layout: str, world: int, rank: int, q_local, k_all, v_all, *, causal: bool = True,

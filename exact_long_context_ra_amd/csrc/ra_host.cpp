@@ -941,10 +941,14 @@ size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t
   return base + ds_bytes_ring(pieces);
 }
 
-ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
-                      ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, const float* lse,
-                      ra_tensor dout, ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+// The ring backward behind ra_ring_bwd and ra_ring_bwd_noalloc.  With
+// side_streams false the fp32 per-sequence rings run one after another on the
+// caller's stream (no side streams or events are created).
+static ra_status ring_bwd_impl(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                               ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
+                               ra_tensor out, const float* lse, ra_tensor dout, ra_tensor dq, ra_tensor dk_ring,
+                               ra_tensor dv_ring, int64_t stride_rank_grad, void* workspace, size_t workspace_bytes,
+                               bool side_streams, void* stream) {
   int64_t L = 0;
   std::vector<Piece> pieces;
   ra_status st = ring_common(prob, layout, world, rank, &L, &pieces);
@@ -1026,7 +1030,8 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     return RA_OK;
   }
   // one ring: on the caller's stream; fp32 sequences: one ring each on side streams
-  const int ns = pieces.size() <= 1 ? 1 : (int)std::min<size_t>(kSideStreams, pieces.size());
+  // (or one after another on the caller's stream)
+  const int ns = (pieces.size() <= 1 || !side_streams) ? 1 : (int)std::min<size_t>(kSideStreams, pieces.size());
   SidePool* pool = nullptr;
   std::vector<int> where(pieces.size(), 0);
   if (ns > 1) {
@@ -1059,11 +1064,48 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
     }
     return RA_OK;
   };
-  if (ns == 1) return run_piece(pieces[0], s, dsT);
+  if (pieces.size() == 1) return run_piece(pieces[0], s, dsT);
+  if (ns == 1) {
+    for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i) st = run_piece(pieces[i], s, nullptr);
+    return st;
+  }
   for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i)
     st = run_piece(pieces[i], pool->st[where[i]], nullptr);
   const ra_status sj = join_streams(pool, ns, s);
   return st != RA_OK ? st : sj;
+}
+
+ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank, ra_tensor q_local,
+                      ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank, ra_tensor out, const float* lse,
+                      ra_tensor dout, ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return ring_bwd_impl(prob, layout, world, rank, q_local, k_ring, v_ring, stride_rank, out, lse, dout, dq, dk_ring,
+                       dv_ring, stride_rank_grad, workspace, workspace_bytes, true, stream);
+}
+
+size_t ra_noalloc_scratch_bytes(void) { return scratch_capacity(); }
+
+ra_status ra_ring_bwd_noalloc(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                              ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
+                              ra_tensor out, const float* lse, ra_tensor dout, ra_tensor dq, ra_tensor dk_ring,
+                              ra_tensor dv_ring, int64_t stride_rank_grad, void* stream) {
+  // Validation and the size check first (host arithmetic only): delta must fit
+  // the fixed scratch.
+  int64_t L = 0;
+  std::vector<Piece> pieces;
+  ra_status st = ring_common(prob, layout, world, rank, &L, &pieces);
+  if (st != RA_OK) return st;
+  if (L == 0) return RA_OK;
+  const size_t cap = scratch_capacity();
+  const size_t need = ra_ring_workspace_min_bytes(prob, layout, world);
+  RA_CHECK(need <= cap, RA_ERR_WORKSPACE,
+           "ra_ring_bwd_noalloc: delta needs %zu bytes, more than the %zu-byte fixed scratch "
+           "(batch*heads*S/N must stay at or below %zu); use ra_ring_bwd with a workspace",
+           need, cap, cap / sizeof(float));
+  void* ptr = nullptr;
+  RA_HIP(scratch_device_ptr(&ptr));
+  return ring_bwd_impl(prob, layout, world, rank, q_local, k_ring, v_ring, stride_rank, out, lse, dout, dq, dk_ring,
+                       dv_ring, stride_rank_grad, ptr, cap, false, stream);
 }
 
 

@@ -130,6 +130,11 @@ hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_cast(const float* src, void* dst, int64_t n, hipStream_t s);
+// Fixed device scratch of the no-allocation entry point (ra_kernels.hip): its
+// size, and its address on the current device (looked up once per device with
+// hipGetSymbolAddress; the array's host-side name is not a device address).
+size_t scratch_capacity();
+hipError_t scratch_device_ptr(void** out);
 hipError_t launch_zero(const Tensor4W& t, int32_t batch, int32_t heads, int32_t rows, int32_t dim,
                        hipStream_t s);
 

@@ -29,6 +29,7 @@
 // visible key interval [lo, hi] follows from the causal flag and cu_seqlens;
 // tiles entirely outside it are skipped, tiles entirely inside it run without
 // any per-element mask, and only the remaining tiles are masked per element.
+#include <mutex>
 #include <type_traits>
 
 #include "ra_internal.h"
@@ -2188,6 +2189,39 @@ __global__ __launch_bounds__(NT) void cast_kernel(const float* src, uint16_t* ds
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + NT - 1) / NT); }
 
 }  // namespace
+
+// ============================================================================================
+// Fixed scratch of ra_ring_bwd_noalloc (callers that cannot allocate): one
+// array per GPU, held until the process ends.  Host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device.
+// ============================================================================================
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+size_t scratch_capacity() { return kScratchBytes; }
+
+hipError_t scratch_device_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // ============================================================================================
 // Launchers

@@ -202,6 +202,26 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
                       ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ra_ring_bwd without a workspace
+ * argument.  Its scratch (delta and, when it also fits, the bf16 dS^T of a step) lives in
+ * a fixed device array of ra_noalloc_scratch_bytes() (32 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends; the call itself allocates
+ * nothing, and nothing in the scratch needs clearing between calls (every value read is
+ * written earlier in the same call).  A problem whose delta (4 * batch * heads * S/N bytes,
+ * rounded up to 256) exceeds the array is rejected with RA_ERR_WORKSPACE before anything
+ * is enqueued; when delta fits but the dS^T does not, dQ comes from the recompute kernel
+ * (ra_ring_bwd's minimal-workspace path).  The fp32 per-sequence layouts run their
+ * sequences one after another on `stream` (no side streams).  Every call on a GPU uses
+ * that GPU's one array: calls that may overlap on one GPU (other streams or threads)
+ * race and must be serialised by the caller.  Other arguments and results as ra_ring_bwd. */
+ra_status ra_ring_bwd_noalloc(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
+                              ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
+                              ra_tensor out, const float* lse, ra_tensor dout,
+                              ra_tensor dq, ra_tensor dk_ring, ra_tensor dv_ring, int64_t stride_rank_grad,
+                              void* stream);
+size_t ra_noalloc_scratch_bytes(void);
+
 /* Bytes of device workspace for ra_ring_bwd's fastest path (0 on invalid input):
  * delta (b*h*L fp32) and, for bf16, dS^T (b*h*round_up(L, 128)^2 bf16), L = S/N;
  * for a per-sequence layout, the sum of that dS^T size over the sequences, each

@@ -189,3 +189,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libra.so"))
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         L.lib()
+
+
+def test_noalloc_rejects_before_any_gpu_call(ra):
+    """The no-allocation backward checks that delta fits its fixed scratch with
+    host arithmetic alone: an oversized problem is refused before any HIP call
+    (this runs without a GPU) and with a message naming the limit."""
+    lib = ra.lib()
+    cap = lib.ra_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    from exact_long_context_ra_amd._lib import ra_problem, ra_tensor
+    p = ra_problem()
+    p.batch, p.heads, p.head_dim, p.dtype, p.causal = 1, 64, 128, 1, 1
+    p.seq_len = 8 * (cap // 4 // 64 + 128)  # delta of S/8 rows x 64 heads x 4 B > cap
+    t = ra_tensor(None, 0, 0, 0)
+    st = lib.ra_ring_bwd_noalloc(C.byref(p), 1, 8, 0, t, t, t, 0, t, None, t, t, t, t, 0, None)
+    assert st == 4  # RA_ERR_WORKSPACE
+    assert b"fixed scratch" in lib.ra_last_error()
