@@ -11,8 +11,14 @@ pairs x 4 * head_dim * heads for the forward and 2.5x that for the backward
 (5 matrix products per pair instead of 2), divided by the measured time.
 Peak: MI355X dense bf16 MFMA, 2516.6 TFLOP/s (256 CU x 4096 FLOP/clk x 2.4 GHz).
 
+Besides the headline workload, the default run also times the other layouts
+(the stripe share, the contiguous ring over all ranks, the packed varlen
+stream over all slices through the ring and through the gathered-K/V share,
+and the per-sequence zigzag / stripe layouts) with a few steps each, reported
+compactly under "other_workloads"; and it samples the GPU clock under load.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload zigzag]
-       [--no-cpu-baseline]
+       [--also LIST|none] [--no-cpu-baseline]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -20,7 +26,10 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -33,16 +42,20 @@ PEAK_BF16_TFLOPS = 2516.6
 METRIC = "attention TFLOP/s (causal-adjusted) fwd and fwd+bwd, % bf16 MFMA peak"
 
 WORKLOADS = {
-    # name: (layout, seq_len, world, ranks timed, varlen)
-    "zigzag": ("zigzag", 131072, 8, [0], False),
-    "stripe": ("stripe", 262144, 8, [0], False),
-    "contiguous": ("contiguous", 32768, 8, list(range(8)), False),
-    "varlen": ("contiguous", 131072, 8, list(range(8)), True),
+    # name: (layout, seq_len, world, ranks timed, varlen, gathered K/V)
+    "zigzag": ("zigzag", 131072, 8, [0], False, False),
+    "stripe": ("stripe", 262144, 8, [0], False, False),
+    "contiguous": ("contiguous", 32768, 8, list(range(8)), False, False),
+    "varlen": ("contiguous", 131072, 8, list(range(8)), True, False),
+    # the same packed sequences, every rank's slice against the whole gathered
+    # K/V in one block step (llama3-style share)
+    "varlen_gathered": ("contiguous", 131072, 8, list(range(8)), True, True),
     # per-sequence layouts: the same packed sequences, each laid out on its own
     # (lengths rounded to multiples of 2N / N); rank 0 (zigzag: every rank equal)
-    "zigzag_varlen": ("zigzag_varlen", 131072, 8, [0], True),
-    "stripe_varlen": ("stripe_varlen", 131072, 8, [0], True),
+    "zigzag_varlen": ("zigzag_varlen", 131072, 8, [0], True, False),
+    "stripe_varlen": ("stripe_varlen", 131072, 8, [0], True, False),
 }
+DEFAULT_ALSO = "stripe,contiguous,varlen,varlen_gathered,zigzag_varlen,stripe_varlen"
 HEADS, HEAD_DIM = 32, 128
 
 
@@ -95,9 +108,12 @@ def cpu_baseline(layout, S, N, r, cu, D, seed=123):
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = sorted({f"{i.get('internal_api')} ({i.get('user_api')})" for i in info})
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+        blas = []
     qpos = oracle.layout_positions(layout, S, N, r, _lcu(layout, cu))
     rows = qpos[::3]
     rng = np.random.default_rng(seed)
@@ -121,7 +137,169 @@ def cpu_baseline(layout, S, N, r, cu, D, seed=123):
                    f"{layout} share ({len(rows)} rows x {S} keys, {pairs} visible pairs), {dt:.1f} s"),
         "seconds": dt,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "os_cpu_count": os.cpu_count(),
+        "blas": blas,
     }
+
+
+class Workload:
+    """Resident inputs, outputs and workspace of one workload, and its step functions."""
+
+    def __init__(self, name, ra, synth, torch, dev):
+        layout, S, N, ranks, varlen, gathered = WORKLOADS[name]
+        self.name, self.layout, self.S, self.N, self.ranks = name, layout, S, N, ranks
+        self.varlen, self.gathered = varlen, gathered
+        self.ra, self.torch = ra, torch
+        H, D = HEADS, HEAD_DIM
+        L = S // N
+        cu = None
+        if varlen:
+            lengths = synth.loguniform_lengths(S, 1024, 32768, seed=0)
+            if layout.endswith("_varlen"):
+                lengths = synth.round_lengths(lengths, 2 * N if layout == "zigzag_varlen" else N)
+            cu = synth.cu_seqlens(lengths)
+        self.cu = cu
+        # Inputs: global Q, K, V, dO drawn on the GPU, laid out into the ring by the
+        # library's positions; all resident before timing.
+        q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=0, device=dev, with_dout=True)
+        idx = [torch.from_numpy(ra.layout_positions(layout, S, N, r, _lcu(layout, cu))).to(dev) for r in range(N)]
+        self.k_ring = torch.stack([k.index_select(1, i) for i in idx]).contiguous()
+        self.v_ring = torch.stack([v.index_select(1, i) for i in idx]).contiguous()
+        del k, v
+        self.q_loc = {r: q.index_select(1, idx[r]).contiguous() for r in ranks}
+        self.do_loc = {r: do.index_select(1, idx[r]).contiguous() for r in ranks}
+        del q, do
+        self.out = {r: torch.empty((1, L, H, D), device=dev, dtype=torch.float32) for r in ranks}
+        self.lse = {r: torch.empty((1, H, L), device=dev, dtype=torch.float32) for r in ranks}
+        self.dq = torch.empty((1, L, H, D), device=dev, dtype=torch.float32)
+        self.dk_ring = torch.zeros(self.k_ring.shape, device=dev, dtype=torch.float32)
+        self.dv_ring = torch.zeros(self.v_ring.shape, device=dev, dtype=torch.float32)
+        if gathered:
+            # contiguous layout: the rank-major ring is the global token order
+            assert layout == "contiguous"
+            self.k_all = self.k_ring.view(1, S, H, D)
+            self.v_all = self.v_ring.view(1, S, H, D)
+            self.dk_all = self.dk_ring.view(1, S, H, D)
+            self.dv_all = self.dv_ring.view(1, S, H, D)
+            nbytes = max(ra.gathered_workspace_bytes(layout, N, r, self.q_loc[ranks[0]], cu_seqlens=cu)
+                         for r in ranks)
+        else:
+            nbytes = ra.ring_workspace_bytes(layout, N, self.q_loc[ranks[0]], cu_seqlens=cu)
+        self.ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+        self.pairs = {r: step_pairs(ra, layout, S, N, r, cu) for r in ranks}
+        self.total_pairs = sum(sum(p) for p in self.pairs.values())
+        self.fwd_flops = 4.0 * D * H * self.total_pairs
+        self.fb_flops = 3.5 * self.fwd_flops
+
+    def fwd(self):
+        ra = self.ra
+        for r in self.ranks:
+            if self.gathered:
+                ra.gathered_fwd(self.layout, self.N, r, self.q_loc[r], self.k_all, self.v_all, causal=True,
+                                cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+            else:
+                ra.ring_fwd(self.layout, self.N, r, self.q_loc[r], self.k_ring, self.v_ring, causal=True,
+                            cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+
+    def step(self):
+        ra = self.ra
+        for r in self.ranks:
+            if self.gathered:
+                ra.gathered_fwd(self.layout, self.N, r, self.q_loc[r], self.k_all, self.v_all, causal=True,
+                                cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+                ra.gathered_bwd(self.layout, self.N, r, self.q_loc[r], self.k_all, self.v_all, self.out[r],
+                                self.lse[r], self.do_loc[r], causal=True, cu_seqlens=self.cu, dq=self.dq,
+                                dk_all=self.dk_all, dv_all=self.dv_all, workspace=self.ws)
+            else:
+                ra.ring_fwd(self.layout, self.N, r, self.q_loc[r], self.k_ring, self.v_ring, causal=True,
+                            cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+                ra.ring_bwd(self.layout, self.N, r, self.q_loc[r], self.k_ring, self.v_ring, self.out[r],
+                            self.lse[r], self.do_loc[r], causal=True, cu_seqlens=self.cu, dq=self.dq,
+                            dk_ring=self.dk_ring, dv_ring=self.dv_ring, workspace=self.ws)
+
+    def describe(self):
+        r0 = self.ranks
+        many = len(r0) > 1
+        return (f"{self.layout} causal {'gathered-K/V (llama3-style) ' if self.gathered else 'ring '}"
+                f"share{'s' if many else ''} "
+                f"{'(varlen, log-uniform lengths in [1024, 32768]) ' if self.varlen else ''}"
+                f"{'(lengths rounded to whole layout chunks) ' if self.layout.endswith('_varlen') else ''}"
+                f"fwd+bwd: seq {self.S}, ring of {self.N}, rank{'s' if many else ''} "
+                f"{r0 if many else r0[0]}, {HEADS} heads, head_dim {HEAD_DIM}, batch 1")
+
+
+def timed_steps(torch, fn, steps):
+    """Per-step milliseconds of `steps` calls of fn, each bracketed by events on
+    the current stream, with a synchronisation before and after the region."""
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        fn()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
+def sample_gfx_clock(torch, fn, seconds=2.0):
+    """Median GFX clock (MHz, mean over the XCDs) that amd-smi reports while fn()
+    runs back to back for about `seconds`; None where amd-smi is unavailable."""
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                                     text=True, timeout=10).stdout
+                data = json.loads(out[out.index("{"):])
+                clk = data["gpu_data"][0]["clock"] if "gpu_data" in data else data[0]["clock"]
+                vals = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)
+                        and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
+                if vals:
+                    samples.append(sum(vals) / len(vals))
+            except Exception:
+                return
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end or (th.is_alive() and not samples and time.perf_counter() < t_end + 10):
+        fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    # drop the first sample (the GPU may still be ramping up)
+    use = samples[1:] if len(samples) > 2 else samples
+    return round(statistics.median(use), 1) if use else None
+
+
+def secondary(name, ra, synth, torch, dev, steps, warmup):
+    """Compact timing of one more workload (fwd and fwd+bwd, `steps` each)."""
+    w = Workload(name, ra, synth, torch, dev)
+    for _ in range(warmup):
+        w.step()
+    fb = timed_steps(torch, w.step, steps)
+    fw = timed_steps(torch, w.fwd, steps)
+    res = {
+        "workload": w.describe(),
+        "ranks": w.ranks,
+        "visible_pairs_per_head": w.total_pairs,
+        "steps": steps,
+        "ms_per_step": round(sum(fb) / steps, 3),
+        "median_ms": round(statistics.median(fb), 3),
+        "min_ms": round(min(fb), 3),
+        "tflops": round(w.fb_flops / (sum(fb) / steps / 1e3) / 1e12, 2),
+        "ms_fwd": round(sum(fw) / steps, 3),
+        "fwd_min_ms": round(min(fw), 3),
+        "fwd_tflops": round(w.fwd_flops / (sum(fw) / steps / 1e3) / 1e12, 2),
+    }
+    res["pct_peak_fwd_bwd"] = round(100 * res["tflops"] / PEAK_BF16_TFLOPS, 2)
+    res["pct_peak_fwd"] = round(100 * res["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -130,6 +308,10 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="zigzag", choices=sorted(WORKLOADS))
+    ap.add_argument("--also", default=DEFAULT_ALSO,
+                    help="comma-separated further workloads timed compactly after the headline ('none': skip)")
+    ap.add_argument("--also-steps", type=int, default=3)
+    ap.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock under load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one plain device copy of MIB MiB (scales the HBM byte counters)")
@@ -154,87 +336,51 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}), flush=True)
         return
-    layout, S, N, ranks, varlen = WORKLOADS[args.workload]
+    w = Workload(args.workload, ra, synth, torch, dev)
     H, D = HEADS, HEAD_DIM
-    L = S // N
-    cu = None
-    if varlen:
-        lengths = synth.loguniform_lengths(S, 1024, 32768, seed=0)
-        if layout.endswith("_varlen"):
-            lengths = synth.round_lengths(lengths, 2 * N if layout == "zigzag_varlen" else N)
-        cu = synth.cu_seqlens(lengths)
+    print(f"bench: {args.workload} inputs resident", file=sys.stderr, flush=True)
 
-    # Inputs: global Q, K, V, dO drawn on the GPU, laid out into the ring by the
-    # library's positions; all resident before timing.
-    q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=0, device=dev, with_dout=True)
-    idx = [torch.from_numpy(ra.layout_positions(layout, S, N, r, _lcu(layout, cu))).to(dev) for r in range(N)]
-    k_ring = torch.stack([k.index_select(1, i) for i in idx]).contiguous()
-    v_ring = torch.stack([v.index_select(1, i) for i in idx]).contiguous()
-    del k, v
-    q_loc = {r: q.index_select(1, idx[r]).contiguous() for r in ranks}
-    do_loc = {r: do.index_select(1, idx[r]).contiguous() for r in ranks}
-    del q, do
-    out = {r: torch.empty((1, L, H, D), device=dev, dtype=torch.float32) for r in ranks}
-    lse = {r: torch.empty((1, H, L), device=dev, dtype=torch.float32) for r in ranks}
-    dq = torch.empty((1, L, H, D), device=dev, dtype=torch.float32)
-    dk_ring = torch.zeros(k_ring.shape, device=dev, dtype=torch.float32)
-    dv_ring = torch.zeros(v_ring.shape, device=dev, dtype=torch.float32)
-    ws = torch.empty(ra.ring_workspace_bytes(layout, N, q_loc[ranks[0]], cu_seqlens=cu), device=dev,
-                     dtype=torch.uint8)
-
-    pairs = {r: step_pairs(ra, layout, S, N, r, cu) for r in ranks}
-    total_pairs = sum(sum(p) for p in pairs.values())
-    fwd_flops = 4.0 * D * H * total_pairs
-    fb_flops = 3.5 * fwd_flops
-
-    def fwd():
-        for r in ranks:
-            ra.ring_fwd(layout, N, r, q_loc[r], k_ring, v_ring, causal=True, cu_seqlens=cu,
-                        out=out[r], lse=lse[r])
-
-    def step():
-        for r in ranks:
-            ra.ring_fwd(layout, N, r, q_loc[r], k_ring, v_ring, causal=True, cu_seqlens=cu,
-                        out=out[r], lse=lse[r])
-            ra.ring_bwd(layout, N, r, q_loc[r], k_ring, v_ring, out[r], lse[r], do_loc[r], causal=True,
-                        cu_seqlens=cu, dq=dq, dk_ring=dk_ring, dv_ring=dv_ring, workspace=ws)
-
-    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        step()
+        w.step()
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, bracketed by synchronisations; per-launch
     # HIP events recorded by the library on the launch stream give each
     # kernel's average duration.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with ra.kernel_timing(capacity=8192) as kt:
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+        step_ms = timed_steps(torch, w.step, args.steps)
+    ms_step = sum(step_ms) / args.steps
 
     # The per-launch event records leave about 10 us between launches; the
     # same K steps without them, reported beside the headline for reference.
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_plain = ev0.elapsed_time(ev1) / args.steps
+    plain_ms = timed_steps(torch, w.step, args.steps)
+    ms_step_plain = sum(plain_ms) / args.steps
 
     # Forward alone (second timed region, same inputs).
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        fwd()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_fwd = ev0.elapsed_time(ev1) / args.steps
+    fwd_ms = timed_steps(torch, w.fwd, args.steps)
+    ms_fwd = sum(fwd_ms) / args.steps
+
+    # Ring efficiency: N x the time of a causal self-attention block step of one
+    # local chunk (the rank's queries against its own keys), over the time of the
+    # rank's whole ring forward.
+    ring_eff = None
+    if not w.gathered and len(w.ranks) == 1 and not w.layout.endswith("_varlen"):
+        r = w.ranks[0]
+        qm = ra.layout_posmap(w.layout, w.S, w.N, r)
+        ob = torch.empty_like(w.out[r])
+        lb = torch.empty_like(w.lse[r])
+
+        def diag():
+            ra.block_attn_fwd(w.q_loc[r], w.k_ring[r], w.v_ring[r], qm, qm, seq_len=w.S, causal=True,
+                              cu_seqlens=w.cu, out_b=ob, lse_b=lb)
+
+        diag()
+        d_ms = timed_steps(torch, diag, max(3, args.steps))
+        t_diag = sum(d_ms) / len(d_ms)
+        ring_eff = {"value": round(w.N * t_diag / ms_fwd, 4), "block_ms": round(t_diag, 4), "ring_fwd_ms": round(ms_fwd, 4),
+                    "definition": "N x time(causal block step of one local chunk against itself) / time(ring forward)"}
+
+    gfx_mhz = None if args.no_clock else sample_gfx_clock(torch, w.step)
 
     # Per-kernel algorithmic FLOPs: each launch of block_fwd / block_bwd covers
     # one ring step of one rank: pairs(step) x 4*D*H (fwd) or x 10*D*H (bwd).
@@ -252,7 +398,7 @@ def main():
     per_pair = {"block_fwd": 4.0, "block_bwd_dkdv": 8.0, "block_bwd_dq_ds": 2.0, "block_bwd_dq": 6.0}
     for name, f in per_pair.items():
         per_kernel.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0})["flops"] = (
-            f * D * H * total_pairs * args.steps)
+            f * D * H * w.total_pairs * args.steps)
     dom = max(per_kernel, key=lambda n: per_kernel[n]["ms"])
     dk = per_kernel[dom]
     if dom in per_pair and dk["ms"] > 0:
@@ -265,8 +411,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": None, "peak": 8000.0, "unit": "GB/s", "frac": None,
                     "traffic": None, "kernel": dom}
 
-    value = fb_flops / (ms_step / 1e3) / 1e12
-    fwd_tflops = fwd_flops / (ms_fwd / 1e3) / 1e12
+    value = w.fb_flops / (ms_step / 1e3) / 1e12
+    fwd_tflops = w.fwd_flops / (ms_fwd / 1e3) / 1e12
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -281,28 +427,48 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (N(0,1) bf16, seeded)",
         "config": {
-            "workload": (f"{layout} causal ring share{'s' if len(ranks) > 1 else ''} "
-                         f"{'(varlen, log-uniform lengths in [1024, 32768]) ' if varlen else ''}"
-                         f"{'(lengths rounded to whole layout chunks) ' if layout.endswith('_varlen') else ''}"
-                         f"fwd+bwd: seq {S}, ring of {N}, rank{'s' if len(ranks) > 1 else ''} "
-                         f"{ranks if len(ranks) > 1 else ranks[0]}, {H} heads, head_dim {D}, batch 1"),
-            "layout": layout, "seq_len": S, "world": N, "ranks": ranks, "heads": H, "head_dim": D,
-            "batch": 1, "causal": True, "varlen": varlen,
+            "workload": w.describe(),
+            "layout": w.layout, "seq_len": w.S, "world": w.N, "ranks": w.ranks, "heads": H, "head_dim": D,
+            "batch": 1, "causal": True, "varlen": w.varlen, "gathered_kv": w.gathered,
         },
         "pct_peak_fwd_bwd": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_tflops, 2),
         "pct_peak_fwd": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
         "ms_fwd": round(ms_fwd, 3),
+        "step_ms_median": round(statistics.median(step_ms), 3),
+        "step_ms_min": round(min(step_ms), 3),
+        "fwd_ms_median": round(statistics.median(fwd_ms), 3),
+        "fwd_ms_min": round(min(fwd_ms), 3),
         "ms_per_step_without_launch_events": round(ms_step_plain, 3),
-        "visible_pairs_per_head": total_pairs,
+        "visible_pairs_per_head": w.total_pairs,
+        "ring_efficiency_fwd": ring_eff,
+        "gfx_clock_mhz_under_load": gfx_mhz,
         "kernels": {n: {"launches": a["launches"], "avg_ms": round(a["ms"] / max(1, a["launches"]), 4),
                         **({"tflops": round(a["flops"] / (a["ms"] / 1e3) / 1e12, 1)} if a["flops"] and a["ms"] else {})}
                     for n, a in per_kernel.items() if a["launches"]},
         "roofline": roofline,
         "cpu_baseline": None,
+        "other_workloads": {},
     }
+    headline = (w.layout, w.S, w.N, list(w.ranks), w.varlen, w.gathered)
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    also = [] if args.also in ("", "none") else [a.strip() for a in args.also.split(",") if a.strip()]
+    for name in also:
+        if name not in WORKLOADS or WORKLOADS[name] == headline:
+            continue
+        print(f"bench: {name}", file=sys.stderr, flush=True)
+        res["other_workloads"][name] = secondary(name, ra, synth, torch, dev, max(1, args.also_steps), 1)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(layout, S, N, ranks[0], cu, D)
+        lay, S, N, ranks, _, _ = WORKLOADS[args.workload]
+        cu = None
+        if WORKLOADS[args.workload][4]:
+            lengths = synth.loguniform_lengths(S, 1024, 32768, seed=0)
+            if lay.endswith("_varlen"):
+                lengths = synth.round_lengths(lengths, 2 * N if lay == "zigzag_varlen" else N)
+            cu = synth.cu_seqlens(lengths)
+        res["cpu_baseline"] = cpu_baseline(lay, S, N, ranks[0], cu, D)
     print(json.dumps(res), flush=True)
 
 

@@ -16,9 +16,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_bench_json_line():
     from gpu_util import log
-    log("bench.py --steps 2 --warmup 1 --no-cpu-baseline")
+    log("bench.py --steps 2 --warmup 1 --no-cpu-baseline --also contiguous --also-steps 1")
     res = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
-                          "--no-cpu-baseline"], capture_output=True, text=True, timeout=240, cwd=ROOT)
+                          "--no-cpu-baseline", "--also", "contiguous", "--also-steps", "1"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-2000:]
     lines = [ln for ln in res.stdout.splitlines() if ln.startswith("{")]
     assert len(lines) == 1, res.stdout[-2000:]
@@ -44,3 +45,12 @@ def test_bench_json_line():
     # the per-kernel launches: 8 ring steps per timed step for each block kernel
     for name in ("block_fwd", "block_bwd_dkdv", "block_bwd_dq_ds"):
         assert r["kernels"][name]["launches"] == 2 * 8, name
+    # step statistics, ring efficiency and the compact line of a further workload
+    assert r["step_ms_min"] <= r["step_ms_median"] and r["fwd_ms_min"] <= r["fwd_ms_median"]
+    re_ = r["ring_efficiency_fwd"]
+    assert re_ is not None and 0 < re_["value"] < 2 and re_["ring_fwd_ms"] == pytest.approx(r["ms_fwd"], rel=1e-3)
+    o = r["other_workloads"]["contiguous"]
+    assert o["visible_pairs_per_head"] == 32768 * 32769 // 2  # all 8 ranks: every causal pair once
+    assert o["steps"] == 1 and o["min_ms"] <= o["median_ms"]
+    assert abs(o["tflops"] - 3.5 * 4 * 128 * 32 * o["visible_pairs_per_head"] / (o["ms_per_step"] / 1e3) / 1e12) \
+        <= 0.01 * o["tflops"]
