@@ -312,6 +312,7 @@ def main():
                     help="comma-separated further workloads timed compactly after the headline ('none': skip)")
     ap.add_argument("--also-steps", type=int, default=3)
     ap.add_argument("--no-clock", action="store_true", help="skip sampling the GPU clock under load")
+    ap.add_argument("--no-ring-eff", action="store_true", help="skip the ring-efficiency block-step timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one plain device copy of MIB MiB (scales the HBM byte counters)")
@@ -364,7 +365,7 @@ def main():
     # local chunk (the rank's queries against its own keys), over the time of the
     # rank's whole ring forward.
     ring_eff = None
-    if not w.gathered and len(w.ranks) == 1 and not w.layout.endswith("_varlen"):
+    if not args.no_ring_eff and not w.gathered and len(w.ranks) == 1 and not w.layout.endswith("_varlen"):
         r = w.ranks[0]
         qm = ra.layout_posmap(w.layout, w.S, w.N, r)
         ob = torch.empty_like(w.out[r])

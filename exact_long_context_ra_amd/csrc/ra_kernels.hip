@@ -1139,18 +1139,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
   const Rsrc rv = make_rsrc(vbase, slice_bytes(a.lk, a.v.st, 2, D));
   const uint32_t qst = (uint32_t)(a.q.st * 2), kst = (uint32_t)(a.k.st * 2), vst = (uint32_t)(a.v.st * 2);
 
+  const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
+  const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
+  const int kbeg = first_ge(a.kmap, wg_f.lo);
+  const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+  // No row of this workgroup sees any key of the block (positions increase with
+  // the row, and so do both ends of a row's visible interval): merging an empty
+  // block leaves out and lse as they are, so such a workgroup touches nothing
+  // unless it must write the first result or the low-precision copy.
+  if (kbeg >= kend && a.mode == FWD_MERGE && a.out_lowp.ptr == nullptr) return;
+
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
     qf[c] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)row * qst + (16 * c + 8 * hf) * 2));
 
   const Bounds rb = row_bounds(a.mask, map_pos(a.qmap, min(row, r_last)));
-  const Bounds wg_f = row_bounds(a.mask, map_pos(a.qmap, r_first));
-  const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
   const Bounds wv_f = row_bounds(a.mask, map_pos(a.qmap, min(w_first, r_last)));
   const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
-  const int kbeg = first_ge(a.kmap, wg_f.lo);
-  const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
   const float sl2 = a.scale_log2;
 
   float m_run = NEG_INF, l_run = 0.f, m_use = 0.f;
@@ -1811,6 +1817,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs ap) {
   const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
   const int kbeg = first_ge(a.kmap, wg_f.lo);
   const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+  if (kbeg >= kend) return;  // no row of the workgroup sees a key: dQ gains nothing
   const float sl2 = a.scale_log2;
 
   f32x16 dq[NDB];
@@ -1949,6 +1956,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
   const Bounds wg_l = row_bounds(a.mask, map_pos(a.qmap, r_last));
   const int kbeg = first_ge(a.kmap, wg_f.lo);
   const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
+  if (kbeg >= kend) return;  // no row of the workgroup sees a key: dQ gains nothing
 
   f32x16 acc[NDB];
 #pragma unroll
