@@ -1158,6 +1158,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
   const Bounds wv_f = row_bounds(a.mask, map_pos(a.qmap, min(w_first, r_last)));
   const Bounds wv_l = row_bounds(a.mask, map_pos(a.qmap, w_last));
   const float sl2 = a.scale_log2;
+  // Key positions increase with the key index, so this lane's row sees the
+  // keys of one index interval, [ja, ja + jspan] (ja far past every key when
+  // it sees none): a tile that the wave's rows do not all see whole is masked
+  // with one unsigned compare per score.
+  int ja = first_ge(a.kmap, rb.lo), jspan = 0;
+  {
+    const int jb = min(a.lk - 1, last_le(a.kmap, rb.hi));
+    if (jb < ja || !wave_has_rows) ja = 1 << 30;
+    else jspan = jb - ja;
+  }
 
   float m_run = NEG_INF, l_run = 0.f, m_use = 0.f;
   f32x16 o[NDB];
@@ -1206,16 +1216,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
     const bool vis = wave_has_rows && kmax >= wv_f.lo && kmin <= wv_l.hi;
     const bool full = vis && (j0 + FBK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
     if (!full) {
-      const bool in0 = j0 < a.kmap.s0.len;
-      const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
-      const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
+      // key index of score (c2, v) = j0 + 8 * hf + 32 * c2 + (v < 8 ? v : v + 8)
+      const int t = j0 + 8 * hf - ja;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int j = j0 + c2 * 32 + reg_row(v, hf);
-          const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
-          const bool ok = vis && (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+          const bool ok = (uint32_t)(t + 32 * c2 + (v < 8 ? v : v + 8)) <= (uint32_t)jspan;
           st[c2][v] = ok ? st[c2][v] : NEG_INF;
         }
     }
