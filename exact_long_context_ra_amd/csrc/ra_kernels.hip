@@ -1496,6 +1496,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
   const Bounds cb = col_bounds(a.mask, map_pos(a.kmap, min(key, k_last)));       // this lane's key
   const Bounds cbf = col_bounds(a.mask, map_pos(a.kmap, min(kw0, k_last)));      // wave's first key
   const Bounds cbl = col_bounds(a.mask, map_pos(a.kmap, kw_last));               // wave's last key
+  // Query positions increase with the row index, so the rows that see this
+  // lane's key are one index interval, [ia, ia + ispan] (ia far past every
+  // row when none does): a block that is not fully visible is masked with one
+  // unsigned compare per score.
+  int ia = first_ge(a.qmap, cb.lo), ispan = 0;
+  {
+    const int ib = min(a.lq - 1, last_le(a.qmap, cb.hi));
+    if (ib < ia || !key_ok) ia = 1 << 30;
+    else ispan = ib - ia;
+  }
 
   dma_tile<D, BWD_BK, 8>(rk, kst, k_first, kv_lds + C::OFF_K, w, lane);
   dma_tile<D, BWD_BK, 8>(rv, vst, k_first, kv_lds + C::OFF_V, w, lane);
@@ -1578,15 +1588,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
       const int rwl = min(a.lq - 1, rw0 + 31);
       bool wave_empty = !wave_has_keys || rw0 > rwl;
       bool wave_full = false;
-      int qp0 = 0, qstr = 1;
       if (!wave_empty) {
         const int qfirst = map_pos(a.qmap, rw0), qlast = map_pos(a.qmap, rwl);
         wave_empty = qlast < cbf.lo || qfirst > cbl.hi;
         wave_full = (kw0 + 32 <= a.lk) && (rw0 + 32 <= a.lq) && qfirst >= cbl.lo && qlast <= cbf.hi;
-        const bool in0 = rw0 < a.qmap.s0.len;
-        const bool one_seg = a.qmap.nseg < 2 || in0 == (rwl < a.qmap.s0.len);
-        qp0 = qfirst;
-        qstr = one_seg ? (in0 ? a.qmap.s0.stride : a.qmap.s1.stride) : 0;  // 0: look each row up
       }
       if (!wave_empty) {
         const int hr0 = qh * 32;
@@ -1629,14 +1634,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
         // visible key (-inf) to +inf, so that exp2 gives 0 for all of them;
         // what follows is the same straight-line code for every tile.
         if (!wave_full) {
-          int hq = 8 * hf;
-          asm volatile("" : "+v"(hq));  // keeps the 16 row indices from being precomputed
+          // row index of score v = rw0 + 8 * hf + 16 * (v >> 3) + (v & 7)
+          const int t = rw0 + 8 * hf - ia;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int qm = hr0 + 16 * (v >> 3) + hq + (v & 7);
-            const int r = qt * BQB + qm;
-            const int qp = qstr ? qp0 + (qm - hr0) * qstr : map_pos(a.qmap, min(r, a.lq - 1));
-            const bool ok = key_ok && r < a.lq && qp >= cb.lo && qp <= cb.hi;
+            const bool ok = (uint32_t)(t + 16 * (v >> 3) + (v & 7)) <= (uint32_t)ispan;
             s[v] = ok ? s[v] : NEG_INF;
           }
 #pragma unroll
