@@ -1949,10 +1949,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
   const int r_first = qt * DQS_ROWS;
   const int r_last = min(a.lq, r_first + DQS_ROWS) - 1;
   const int w_first = r_first + 32 * w;
-  const bool wave_has_rows = w_first <= r_last;
   const int row = w_first + l32;
   const bool row_ok = row <= r_last;
-  const int my_qtile = w_first / BQB;  // the dK/dV kernel's query tile holding this wave's rows
 
   const char* kbase = reinterpret_cast<const char*>(a.k.ptr) + (b * a.k.sb + head * a.k.sh) * 2;
   const Rsrc rk = make_rsrc(kbase, slice_bytes(a.lk, a.k.st, 2, D));
@@ -1966,6 +1964,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
   const int kbeg = first_ge(a.kmap, wg_f.lo);
   const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
   if (kbeg >= kend) return;  // no row of the workgroup sees a key: dQ gains nothing
+  // The keys this lane's row sees form one index interval [ja, jb] (key
+  // positions increase with the index); empty for lanes past the last row.
+  // A wave multiplies a tile only when one of its rows sees one of the
+  // tile's keys.  The dK/dV kernel has then visited that block of dS^T (a
+  // row that sees a key lies in the query range it walks for the key's tile),
+  // so only written blocks are used; every other block's dS is zero for
+  // these rows.  The test needs no memory access inside the loop.
+  int ja = 1 << 30, jb = -1;
+  if (row_ok) {
+    const Bounds rbd = row_bounds(a.mask, map_pos(a.qmap, row));
+    ja = first_ge(a.kmap, rbd.lo);
+    jb = min(a.lk - 1, last_le(a.kmap, rbd.hi));
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -2016,22 +2027,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
 
   if (kbeg < kend) {
     const int jt0 = kbeg / DQ_BK, jt1 = (kend - 1) / DQ_BK;
-    int cov_tile = -1;
-    bool covered = false;
     // Tile jt from `cur` while tile jt + 2 is fetched into `nxt2` (which held
     // tile jt - 1); at the end, wait until tile jt + 1 has landed, leaving tile
     // jt + 2 in flight.  Past the last tile the last one is fetched again into
     // the free buffer, so that every step issues the same copies.
     auto step = [&](int jt, const char* cur, char* nxt2) {
       issue(min(jt + 2, jt1), nxt2);
-      const int kt = jt * DQ_BK / BWD_BK;
-      if (kt != cov_tile) {
-        int q0, q1;
-        dkdv_query_tiles(a, kt, q0, q1);
-        covered = my_qtile >= q0 && my_qtile <= q1;
-        cov_tile = kt;
-      }
-      if (wave_has_rows && covered) {
+      if (__any(ja <= jt * DQ_BK + DQ_BK - 1 && jb >= jt * DQ_BK)) {
 #pragma unroll
         for (int ks = 0; ks < DQ_BK / 16; ++ks) {
           const u32x2 slo = tr16(cur + offS[0] + ks * 16 * 256), shi = tr16(cur + offS[1] + ks * 16 * 256);
