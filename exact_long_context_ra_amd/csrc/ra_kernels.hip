@@ -1332,9 +1332,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
   }
   float* lse_p = a.lse + ((int64_t)b * a.heads + head) * a.lse_sh + row;
   float* orow = reinterpret_cast<float*>(a.out.ptr) + b * a.out.sb + (int64_t)row * a.out.st + head * a.out.sh;
+  // The running output's 16 vectors of this lane are all read before any
+  // store, so that their reads are in flight together (read one by one
+  // between the stores, each waited for its own round trip).
+  f32x4 prev[NDB][4];
+  float lse_old = 0.f;
+  if (a.mode == FWD_MERGE) {
+    lse_old = *lse_p;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) prev[d][g] = *reinterpret_cast<const f32x4*>(orow + d * 32 + 8 * g + 4 * hf);
+  }
   float wa = 0.f, wb = inv, lse_new = lse_b;
   if (a.mode == FWD_MERGE) {
-    const float lse_old = *lse_p;
     const float mm = fmaxf(lse_old, lse_b);
     if (mm == NEG_INF) {
       wa = 0.f;
@@ -1354,7 +1365,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
     for (int g = 0; g < 4; ++g) {
       const int d0 = d * 32 + 8 * g + 4 * hf;
       f32x4 val = {o[d][4 * g] * wb, o[d][4 * g + 1] * wb, o[d][4 * g + 2] * wb, o[d][4 * g + 3] * wb};
-      if (a.mode == FWD_MERGE) val += wa * *reinterpret_cast<const f32x4*>(orow + d0);
+      if (a.mode == FWD_MERGE) val += wa * prev[d][g];
       *reinterpret_cast<f32x4*>(orow + d0) = val;
       if (a.out_lowp.ptr) {
         uint16_t* lp = reinterpret_cast<uint16_t*>(a.out_lowp.ptr) + b * a.out_lowp.sb +
