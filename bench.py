@@ -159,6 +159,9 @@ class Workload:
                 lengths = synth.round_lengths(lengths, 2 * N if layout == "zigzag_varlen" else N)
             cu = synth.cu_seqlens(lengths)
         self.cu = cu
+        # host and device copies made once: a plain array would be copied to the
+        # device (and the stream waited for) on every call
+        self.cu_arg = ra.CuSeqlens(cu, dev) if cu is not None else None
         # Inputs: global Q, K, V, dO drawn on the GPU, laid out into the ring by the
         # library's positions; all resident before timing.
         q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=0, device=dev, with_dout=True)
@@ -196,25 +199,25 @@ class Workload:
         for r in self.ranks:
             if self.gathered:
                 ra.gathered_fwd(self.layout, self.N, r, self.q_loc[r], self.k_all, self.v_all, causal=True,
-                                cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+                                cu_seqlens=self.cu_arg, out=self.out[r], lse=self.lse[r])
             else:
                 ra.ring_fwd(self.layout, self.N, r, self.q_loc[r], self.k_ring, self.v_ring, causal=True,
-                            cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+                            cu_seqlens=self.cu_arg, out=self.out[r], lse=self.lse[r])
 
     def step(self):
         ra = self.ra
         for r in self.ranks:
             if self.gathered:
                 ra.gathered_fwd(self.layout, self.N, r, self.q_loc[r], self.k_all, self.v_all, causal=True,
-                                cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+                                cu_seqlens=self.cu_arg, out=self.out[r], lse=self.lse[r])
                 ra.gathered_bwd(self.layout, self.N, r, self.q_loc[r], self.k_all, self.v_all, self.out[r],
-                                self.lse[r], self.do_loc[r], causal=True, cu_seqlens=self.cu, dq=self.dq,
+                                self.lse[r], self.do_loc[r], causal=True, cu_seqlens=self.cu_arg, dq=self.dq,
                                 dk_all=self.dk_all, dv_all=self.dv_all, workspace=self.ws)
             else:
                 ra.ring_fwd(self.layout, self.N, r, self.q_loc[r], self.k_ring, self.v_ring, causal=True,
-                            cu_seqlens=self.cu, out=self.out[r], lse=self.lse[r])
+                            cu_seqlens=self.cu_arg, out=self.out[r], lse=self.lse[r])
                 ra.ring_bwd(self.layout, self.N, r, self.q_loc[r], self.k_ring, self.v_ring, self.out[r],
-                            self.lse[r], self.do_loc[r], causal=True, cu_seqlens=self.cu, dq=self.dq,
+                            self.lse[r], self.do_loc[r], causal=True, cu_seqlens=self.cu_arg, dq=self.dq,
                             dk_ring=self.dk_ring, dv_ring=self.dv_ring, workspace=self.ws)
 
     def describe(self):
@@ -373,7 +376,7 @@ def main():
 
         def diag():
             ra.block_attn_fwd(w.q_loc[r], w.k_ring[r], w.v_ring[r], qm, qm, seq_len=w.S, causal=True,
-                              cu_seqlens=w.cu, out_b=ob, lse_b=lb)
+                              cu_seqlens=w.cu_arg, out_b=ob, lse_b=lb)
 
         diag()
         d_ms = timed_steps(torch, diag, max(3, args.steps))

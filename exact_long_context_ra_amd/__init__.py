@@ -4,7 +4,7 @@ The computation lives in the HIP library ``libra.so`` (C ABI: include/ra.h);
 this package only loads it and marshals torch tensors into its calls.
 """
 from .api import (  # noqa: F401
-    LAYOUTS, KernelTimes, block_attn_bwd, block_attn_fwd, bwd_preprocess, cast_f32_to_bf16,
+    LAYOUTS, CuSeqlens, KernelTimes, block_attn_bwd, block_attn_fwd, bwd_preprocess, cast_f32_to_bf16,
     gathered_bwd, gathered_fwd, gathered_workspace_bytes, kernel_timing, layout_positions, layout_posmap,
     lse_merge, noalloc_scratch_bytes, posmap, ring_bwd, ring_bwd_noalloc, ring_fwd, ring_workspace_bytes,
 )

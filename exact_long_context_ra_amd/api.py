@@ -64,6 +64,38 @@ def _stream() -> int:
     return _torch().cuda.current_stream().cuda_stream
 
 
+class CuSeqlens:
+    """cu_seqlens (int32 offsets [0, l0, l0+l1, ...]) held once on the host and once on
+    ``device``.  The library takes both copies (the host one plans the ring steps and
+    splits the per-sequence layouts; the kernels read the device one).  Given a plain
+    list, array or tensor instead, every call makes the missing copy itself, and copying
+    a device tensor to the host waits for the stream; build this once and pass it to
+    every call that uses the same sequences."""
+
+    def __init__(self, cu_seqlens, device):
+        torch = _torch()
+        if isinstance(cu_seqlens, CuSeqlens):
+            cu_seqlens = cu_seqlens.host
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+        self.host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        if self.host.ndim != 1 or self.host.size < 2:
+            raise ValueError("cu_seqlens must hold at least two offsets")
+        self.dev = torch.from_numpy(self.host.copy()).to(device)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.host.size) - 1
+
+
+def _host_cu(cu_seqlens):
+    """The host int32 array of any accepted cu_seqlens form."""
+    if isinstance(cu_seqlens, CuSeqlens):
+        return cu_seqlens.host
+    return np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+                                           dtype=np.int32))
+
+
 class _Cu:
     """Keeps the device and host copies of cu_seqlens alive for a call."""
 
@@ -73,6 +105,11 @@ class _Cu:
         self.host = None
         self.n = 0
         if cu_seqlens is None:
+            return
+        if isinstance(cu_seqlens, CuSeqlens):
+            if cu_seqlens.dev.device != torch.device(device):
+                raise ValueError("CuSeqlens was built for another device")
+            self.host, self.dev, self.n = cu_seqlens.host, cu_seqlens.dev, cu_seqlens.num_seqs
             return
         if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
             # the host copy lets the library skip steps and split per-sequence layouts
@@ -117,8 +154,7 @@ def layout_positions(layout: str, seq_len: int, world: int, rank: int, cu_seqlen
         check(lib().ra_layout_positions(_layout_id(layout), seq_len, world, rank,
                                         out.ctypes.data_as(C.POINTER(C.c_int64))))
         return out
-    cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
-                                         dtype=np.int32))
+    cu = _host_cu(cu_seqlens)
     if int(cu[-1]) != seq_len:
         raise ValueError("cu_seqlens must end at seq_len")
     check(lib().ra_layout_positions_cu(_layout_id(layout), cu.ctypes.data_as(C.POINTER(C.c_int32)), len(cu) - 1,

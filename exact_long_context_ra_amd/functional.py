@@ -48,6 +48,14 @@ def _lowp(x32, dtype):
     raise TypeError(f"unsupported dtype {dtype} (bf16 or fp32)")
 
 
+def _cu_once(cu_seqlens, device):
+    """Host and device copies of cu_seqlens made once for all the calls of one
+    forward and backward (None stays None)."""
+    if cu_seqlens is None or isinstance(cu_seqlens, api.CuSeqlens):
+        return cu_seqlens
+    return api.CuSeqlens(cu_seqlens, device)
+
+
 def _positions(layout: str, S: int, world: int, device, cu_seqlens=None):
     torch = _torch()
     cu = cu_seqlens if layout.endswith("_varlen") else None  # only the per-sequence layouts use it
@@ -106,6 +114,7 @@ def _make_function():
     class RingAttentionFn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q, k, v, layout, world, causal, cu_seqlens, scale):
+            cu_seqlens = _cu_once(cu_seqlens, q.device)
             out, lse, saved = _VirtualRing.forward(q.detach(), k.detach(), v.detach(), layout, world, causal,
                                                    cu_seqlens, scale)
             ctx.saved = saved
@@ -182,6 +191,7 @@ def _make_gathered_function():
         @staticmethod
         def forward(ctx, q_local, k_all, v_all, layout, world, rank, causal, cu_seqlens, scale):
             q_local, k_all, v_all = q_local.detach(), k_all.detach(), v_all.detach()
+            cu_seqlens = _cu_once(cu_seqlens, q_local.device)
             lowp = q_local.dtype != torch.float32
             o32, lse, olp = api.gathered_fwd(layout, world, rank, q_local, k_all, v_all, causal=causal,
                                              cu_seqlens=cu_seqlens, scale=scale, want_lowp=lowp)
@@ -229,6 +239,7 @@ def _make_gathered_group_function():
         @staticmethod
         def forward(ctx, q, k, v, layout, world, causal, cu_seqlens, scale):
             q, k, v = q.detach(), k.detach(), v.detach()
+            cu_seqlens = _cu_once(cu_seqlens, q.device)
             b, S, h, d = q.shape
             idx = _positions(layout, S, world, q.device)
             lowp = q.dtype != torch.float32

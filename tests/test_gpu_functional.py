@@ -225,3 +225,31 @@ def test_gathered_attn_func_matches_ring(layout):
         check_grad(f64(dq), gq, True, what="dq")
         check_grad(f64(dk), gk, True, what="dk")
         check_grad(f64(dv), gv, True, what="dv")
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag_varlen"])
+def test_cu_seqlens_holder_same_results(layout):
+    """ra.CuSeqlens (host and device copies made once) gives the same bits as a
+    plain cu_seqlens array in the ring forward and backward."""
+    import torch
+    ra = _ra()
+    log(f"CuSeqlens holder {layout}")
+    N = 4
+    lengths = [8, 24, 200, 8, 72] if layout == "zigzag_varlen" else [7, 1, 300, 129, 1, 586]
+    S, H, D = sum(lengths), 2, 128
+    cu = synth.cu_seqlens(lengths)
+    holder = ra.CuSeqlens(cu, dev())
+    q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=48, device=dev(), with_dout=True)
+    idx = [torch.from_numpy(ra.layout_positions(layout, S, N, r, holder)).to(dev()) for r in range(N)]
+    k_ring = torch.stack([k.index_select(1, i) for i in idx]).contiguous()
+    v_ring = torch.stack([v.index_select(1, i) for i in idx]).contiguous()
+    r = 1
+    ql, dol = q.index_select(1, idx[r]).contiguous(), do.index_select(1, idx[r]).contiguous()
+    res = []
+    for c in (cu, holder):
+        o, l, _ = ra.ring_fwd(layout, N, r, ql, k_ring, v_ring, cu_seqlens=c)
+        dq, dk, dv = ra.ring_bwd(layout, N, r, ql, k_ring, v_ring, o, l, dol, cu_seqlens=c)
+        res.append((o, l, dq, dk, dv))
+    torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
