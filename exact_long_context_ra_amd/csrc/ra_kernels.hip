@@ -84,15 +84,18 @@ __device__ __forceinline__ int tr_off(int row, int col) {
 __device__ __forceinline__ int map_pos(const DMap& m, int a) {
   return (a < m.s0.len) ? m.s0.begin + a * m.s0.stride : m.s1.begin + (a - m.s0.len) * m.s1.stride;
 }
+// Unit-stride segments (contiguous and zigzag chunks) need no division.
 __device__ __forceinline__ int seg_first_ge(const DSeg& s, int P) {
   if (s.len <= 0) return 0;
   if (P <= s.begin) return 0;
+  if (s.stride == 1) return min(P - s.begin, s.len);
   long long last = (long long)s.begin + (long long)(s.len - 1) * s.stride;
   if (last < P) return s.len;
   return (int)(((long long)P - s.begin + s.stride - 1) / s.stride);
 }
 __device__ __forceinline__ int seg_last_le(const DSeg& s, int P) {
   if (s.len <= 0 || P < s.begin) return -1;
+  if (s.stride == 1) return min(P - s.begin, s.len - 1);
   long long i = ((long long)P - s.begin) / s.stride;
   return (int)(i < s.len - 1 ? i : s.len - 1);
 }
