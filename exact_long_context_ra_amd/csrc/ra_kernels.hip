@@ -1434,12 +1434,15 @@ struct DkdvB {
   static constexpr int NW = 8;                    // waves: 4 key groups x 2 query halves
   static constexpr int TILE = BQB * D * 2;        // one Q (or dO) tile
   static constexpr int OFF_DO = TILE;
-  static constexpr int OFF_LSE = 2 * TILE;        // 64 lse values (natural log, as given)
-  static constexpr int OFF_DEL = OFF_LSE + BQB * 4;
-  static constexpr int BUF = OFF_DEL + BQB * 4;
+  static constexpr int BUF = 2 * TILE;            // a query tile's Q and dO
   static constexpr int NBUF = 2;                  // query tiles are fetched one ahead
-  // The K and V tiles come first, so that a V address is the matching K
-  // address plus an immediate offset that fits the LDS instruction.
+  static constexpr int OFF_DEL = BQB * 4;         // lse (natural log, as given), then delta
+  static constexpr int LSD = 2 * BQB * 4;
+  // The two query buffers come first in LDS (64 KiB for D = 128): every read
+  // of them is one per-lane register plus an immediate below 64 KiB, which is
+  // what the LDS instruction's offset field holds.  The K and V tiles follow;
+  // their read addresses do not change over the loop, and a V address is the
+  // matching K address plus an immediate.
   static constexpr int OFF_K = 0;                 // this workgroup's K tile (BWD_BK rows)
   static constexpr int OFF_V = BWD_BK * D * 2;    // and its V tile
 };
@@ -1461,9 +1464,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
   // The K/V tiles and the two query-tile buffers are three LDS objects, each
   // buffer reached statically: a read of one buffer then does not wait for
   // the DMA filling the other (the compiler cannot otherwise tell them apart).
+  // (the compiler places LDS objects by alignment first: the query buffers'
+  // alignment of a whole buffer puts them at the start)
+  __shared__ __attribute__((aligned(C::BUF))) char qbuf0[C::BUF];
+  __shared__ __attribute__((aligned(C::BUF))) char qbuf1[C::BUF];
   __shared__ __attribute__((aligned(16))) char kv_lds[2 * BWD_BK * D * 2];
-  __shared__ __attribute__((aligned(16))) char qbuf0[C::BUF];
-  __shared__ __attribute__((aligned(16))) char qbuf1[C::BUF];
+  __shared__ __attribute__((aligned(16))) char lsd0[C::LSD];
+  __shared__ __attribute__((aligned(16))) char lsd1[C::LSD];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1558,12 +1565,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
 
-  auto issue = [&](int qtile, char* nb) {
+  auto issue = [&](int qtile, char* nb, char* nl) {
     const int r0 = qtile * BQB;
     dma_tile<D, BQB, 8>(rq, qst, r0, nb, w, lane);
     dma_tile<D, BQB, 8>(rdo, dst, r0, nb + C::OFF_DO, w, lane);
-    if (w == 0) dma_f32x64(rlse, r0, nb + C::OFF_LSE, lane);
-    if (w == 1) dma_f32x64(rdel, r0, nb + C::OFF_DEL, lane);
+    if (w == 0) dma_f32x64(rlse, r0, nl, lane);
+    if (w == 1) dma_f32x64(rdel, r0, nl + C::OFF_DEL, lane);
   };
 
   // dS^T of a tile is stored at the start of the next one: the wait at the end
@@ -1586,17 +1593,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
   };
 
   if (qt0 <= qt1) {
-    issue(qt0, qbuf0);
+    issue(qt0, qbuf0, lsd0);
     wait_vmem();
     __syncthreads();
-    // query tile qt from `buf` while tile qt + 1 is fetched into `nbuf`
-    auto step = [&](int qt, const char* buf, char* nbuf) {
+    // query tile qt from `buf`/`lbuf` while tile qt + 1 is fetched into `nbuf`/`nlbuf`
+    auto step = [&](int qt, const char* buf, const char* lbuf, char* nbuf, char* nlbuf) {
       flush();
-      if (qt + 1 <= qt1) issue(qt + 1, nbuf);
+      if (qt + 1 <= qt1) issue(qt + 1, nbuf, nlbuf);
       const char* sQ = buf;
       const char* sDO = buf + C::OFF_DO;
-      const float* sLse = reinterpret_cast<const float*>(buf + C::OFF_LSE);
-      const float* sDel = reinterpret_cast<const float*>(buf + C::OFF_DEL);
+      const float* sLse = reinterpret_cast<const float*>(lbuf);
+      const float* sDel = reinterpret_cast<const float*>(lbuf + C::OFF_DEL);
       // this wave's 32 query rows of the tile
       const int rw0 = qt * BQB + qh * 32;
       const int rwl = min(a.lq - 1, rw0 + 31);
@@ -1713,8 +1720,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
       __syncthreads();
     };
     for (int qt = qt0; qt <= qt1; qt += 2) {
-      step(qt, qbuf0, qbuf1);
-      if (qt + 1 <= qt1) step(qt + 1, qbuf1, qbuf0);
+      step(qt, qbuf0, lsd0, qbuf1, lsd1);
+      if (qt + 1 <= qt1) step(qt + 1, qbuf1, lsd1, qbuf0, lsd0);
     }
     flush();
   }
