@@ -79,6 +79,8 @@ RING_BWD_CASES = [
     ("zigzag", 800, 4, 2, 64, "bf16", None),
     ("contiguous", 1536, 4, 2, 128, "bf16", "varlen"),
     ("stripe", 1536, 4, 2, 128, "f32", "varlen"),
+    ("zigzag", 1536, 4, 2, 128, "bf16", "varlen"),   # two-segment posmaps with sequence boundaries
+    ("stripe", 1536, 8, 2, 64, "bf16", "varlen"),    # strided posmaps with sequence boundaries
     ("zigzag_varlen", 1536, 4, 2, 128, "bf16", "varlen"),
     ("stripe_varlen", 1536, 4, 2, 64, "bf16", "varlen"),
     ("zigzag_varlen", 1536, 4, 2, 64, "f32", "varlen"),

@@ -106,6 +106,8 @@ RING_CASES = [
     ("contiguous", 1536, 4, 2, 128, "bf16", True, "varlen", 1),
     ("zigzag", 1536, 4, 2, 128, "f32", True, "varlen", 1),
     ("stripe", 1536, 4, 2, 64, "bf16", True, "varlen", 1),
+    ("zigzag", 1536, 4, 2, 128, "bf16", True, "varlen", 1),    # two-segment posmaps and sequence boundaries
+    ("stripe", 1536, 4, 2, 128, "bf16", False, "varlen", 1),   # strided keys, each row sees its whole sequence
     # per-sequence layouts: every sequence zigzagged / striped on its own
     ("zigzag_varlen", 1536, 4, 2, 128, "bf16", True, "varlen", 1),
     ("zigzag_varlen", 1536, 4, 2, 64, "f32", True, "varlen", 1),
