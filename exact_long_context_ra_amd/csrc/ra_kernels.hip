@@ -1091,10 +1091,11 @@ __device__ __forceinline__ void dma_f32x64(Rsrc rs, int first, char* dst, int la
 
 // ============================================================================================
 // bf16 forward, software-pipelined over tiles of 64 keys: while a wave turns
-// S of tile j into P (exponentials) and adds P V into O, it already issues the
-// MFMAs of S for tile j + 1, so that the matrix unit has work during the
-// softmax.  K tiles are therefore DMA'd two tiles ahead and V tiles one ahead,
-// each into the other of two LDS buffers; one barrier per tile.
+// S of tile j into P (exponentials), it already issues the MFMAs of S for
+// tile j + 1, so that the matrix unit has work during the softmax; P V is
+// added into O after a barrier in the middle of the step.  K tiles are
+// therefore DMA'd two tiles ahead and V tiles one ahead, each into the other
+// of two LDS buffers; a V tile has one and a half steps to land, a K tile one.
 // ============================================================================================
 
 template <int D>
@@ -1246,9 +1247,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
     }
     m_use = (m_run == NEG_INF) ? 0.f : m_run;
   };
-  // P = exp2(S * scale*log2(e) - m) for the finished tile, its row sums, and
-  // O^T += V^T P^T (V^T through the transposed read of the natural V tile).
-  auto p_v = [&](f32x16* st, const char* sV) {
+  // P = exp2(S * scale*log2(e) - m) for the finished tile as bf16 operands, and
+  // its row sums; then, once the V tile has landed, O^T += V^T P^T (V^T through
+  // the transposed read of the natural V tile).
+  auto p_only = [&](f32x16* st, bf16x8* pb) {
     float rs = 0.f;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
@@ -1262,15 +1264,20 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pb;
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)st[c2][8 * u + i];
+        for (int q = 0; q < 8; ++q) pb[2 * c2 + u][q] = (__bf16)st[c2][8 * u + q];
+  };
+  auto pv_only = [&](const bf16x8* pb, const char* sV) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
         const int kb0 = (c2 * 32 + 16 * u) * 2 * D;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
           const u32x2 lo = tr16(sV + offV[d][0] + kb0), hi = tr16(sV + offV[d][1] + kb0);
-          o[d] = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, o[d]);
+          o[d] = mfma_bf16(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[2 * c2 + u], o[d]);
         }
       }
   };
@@ -1300,21 +1307,30 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
       asm volatile("" : "+v"(c16), "+v"(lks), "+v"(lvs));
       // Past the end the last tile is fetched again into the free buffer, so
       // that the copies stay in the block of MFMAs; there they are spread one
-      // per two MFMAs (all of a workgroup's copies at once queue up in the
-      // vector-memory path and hold the waves that issue them).
-      dma_tile_lean<D, FBK>(rv, vst, min(jt + 1, jt1) * FBK, dV, w, c16, lvs);
+      // per MFMA (all of a workgroup's copies at once queue up in the
+      // vector-memory path and hold the waves that issue them).  K first: at
+      // the end of the step only this K copy is waited for, while the V copy
+      // has until the middle of the next step (the last copy of a step to land
+      // is what a wave waits for).
       dma_tile_lean<D, FBK>(rk, kst, min(jt + 2, jt1) * FBK, dK, w, c16, lks);
+      dma_tile_lean<D, FBK>(rv, vst, min(jt + 1, jt1) * FBK, dV, w, c16, lvs);
       s_tile(sKn, nxt);
-      p_v(cur, sV);
+      bf16x8 pb[4];
+      p_only(cur, pb);
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // K operands of the first two k-steps
 #pragma unroll
       for (int g = 0; g < 2 * (FBK / (1024 / (2 * D))) / 4; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one buffer->LDS copy
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // operands two k-steps ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // operands two k-steps ahead
       }
-      wait_vmem();
+      // V of this tile (copied during the previous step): every copy issued
+      // before this step's two has landed, in every wave after the barrier
+      wait_vmem_keep<2 * (FBK / 4) / (1024 / (2 * D))>();
+      barrier_keep_vmem();
+      pv_only(pb, sV);
       if (jt + 1 <= jt1) mask_max(jt + 1, nxt);
+      wait_vmem_keep<(FBK / 4) / (1024 / (2 * D))>();     // this step's K copy, not its V copy
       barrier_keep_vmem();
     };
     for (int jt = jt0; jt <= jt1; jt += 2) {
@@ -1323,6 +1339,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
     }
   }
 
+  wait_vmem();  // the last V copy: no copy into LDS may outlive the workgroup
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   float lse_b, inv;
