@@ -79,6 +79,21 @@ __device__ __forceinline__ int tr_off(int row, int col) {
   return row * 128 + ((((col >> 3) ^ sw)) << 4) + ((col & 7) << 1);
 }
 
+// Value of lane l ^ 32 combined with lane l's own, for both halves of the
+// wave at once: v_permlane32_swap exchanges the upper 32 lanes of one register
+// with the lower 32 of another, so swapping a copy with itself gives every lane
+// the pair (x[l], x[l ^ 32]) in its two results, in VALU time (a cross-lane
+// read through the LDS crossbar would sit on the path from the scores to the
+// exponentials).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // ---- posmaps and visibility ---------------------------------------------------------------
 
 __device__ __forceinline__ int map_pos(const DMap& m, int a) {
@@ -375,7 +390,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int j0, const char* s
   for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  mx = max_halves(mx) * sl2;
   // Lazy rescale: the running max only moves when a row max exceeds it by
   // more than RESCALE_TH (so P <= 2^RESCALE_TH); the result is exact either way.
   const bool grow = mx > m_run + RESCALE_TH;
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
   }
 
   // Epilogue: block-normalise, then store or merge into the fp32 running state.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (!row_ok) return;
   float lse_b, inv;
   if (l_tot > 0.f) {
@@ -1235,7 +1250,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, st[c2][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    mx = max_halves(mx) * sl2;
     const bool grow = mx > m_run + RESCALE_TH;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -1340,7 +1355,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
   }
 
   wait_vmem();  // the last V copy: no copy into LDS may outlive the workgroup
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (!row_ok) return;
   float lse_b, inv;
   if (l_tot > 0.f) {
