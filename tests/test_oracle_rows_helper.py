@@ -1,4 +1,4 @@
-"""The threaded row-block driver of the oracle (gpu_util.oracle_rows_fwd_bwd),
+"""The threaded row-block helper of the oracle (gpu_util.oracle_rows_fwd_bwd),
 which the full-size GPU tests use to check whole heads, gives the same results
 as one call of the oracle over the whole key set (it only hands each row block
 the keys that block can see, and adds the blocks' dK/dV contributions)."""
