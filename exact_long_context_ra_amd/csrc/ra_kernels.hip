@@ -1881,6 +1881,14 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs ap) {
   const int kend = min(a.lk, last_le(a.kmap, wg_l.hi) + 1);
   if (kbeg >= kend) return;  // no row of the workgroup sees a key: dQ gains nothing
   const float sl2 = a.scale_log2;
+  // The keys this lane's row sees: one index interval [ja, ja + jspan] (key
+  // positions increase with the index; ja far past every key when none).
+  int ja = first_ge(a.kmap, rb.lo), jspan = 0;
+  {
+    const int jb = min(a.lk - 1, last_le(a.kmap, rb.hi));
+    if (jb < ja || !wave_has_rows) ja = 1 << 30;
+    else jspan = jb - ja;
+  }
 
   f32x16 dq[NDB];
 #pragma unroll
@@ -1906,9 +1914,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs ap) {
       const int kmin = map_pos(a.kmap, j0), kmax = map_pos(a.kmap, jl);
       if (wave_has_rows && kmax >= wv_f.lo && kmin <= wv_l.hi) {
         const bool wave_full = (j0 + DQ_BK <= a.lk) && kmin >= wv_l.lo && kmax <= wv_f.hi;
-        const bool in0 = j0 < a.kmap.s0.len;
-        const bool one_seg = a.kmap.nseg < 2 || in0 == (jl < a.kmap.s0.len);
-        const int kstr = in0 ? a.kmap.s0.stride : a.kmap.s1.stride;
+        const int t = j0 + 8 * hf - ja;  // key index of score (c2, v) = j0 + 8 * hf + 32 * c2 + (v < 8 ? v : v + 8)
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           f32x16 st = f32x16{}, dpt = f32x16{};
@@ -1922,9 +1928,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs ap) {
           for (int v = 0; v < 16; ++v) {
             float e = ex2(__builtin_fmaf(st[v], sl2, -lse2));
             if (!wave_full) {
-              const int j = j0 + c2 * 32 + reg_row(v, hf);
-              const int kp = one_seg ? kmin + (j - j0) * kstr : map_pos(a.kmap, min(j, jl));
-              const bool ok = (j <= jl) && kp >= rb.lo && kp <= rb.hi;
+              const bool ok = (uint32_t)(t + 32 * c2 + (v < 8 ? v : v + 8)) <= (uint32_t)jspan;
               e = ok ? e : 0.f;
             }
             ds[v] = e * (dpt[v] - dl);
