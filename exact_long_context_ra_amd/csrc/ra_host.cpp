@@ -907,16 +907,6 @@ static size_t ds_bytes_sum(const std::vector<Piece>& pieces) {
   return sum;
 }
 
-// Every piece must fit the stored-dS path for it to be used (0 otherwise).
-static size_t ds_bytes_max(const std::vector<Piece>& pieces) {
-  size_t m = 0;
-  for (const Piece& pc : pieces) {
-    const size_t b = ds_bytes(&pc.prob, pc.L);
-    if (b == 0) return 0;
-    m = b > m ? b : m;
-  }
-  return m;
-}
 
 size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
   int64_t L = 0;
@@ -926,10 +916,69 @@ size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int
   return (bytes + 255) & ~(size_t)255;
 }
 
-// dS^T bytes of the stored-dS path: one piece's, or every piece's side by side
-// for the grouped launches of a per-sequence layout (bf16; fp32 stores none).
+// A block's keys can also go through the stored-dS path a chunk at a time:
+// for each chunk of keys the dK/dV kernel writes that chunk's dS^T and the dQ
+// kernel adds its dS K into dQ, so the dS^T buffer holds one chunk (dK/dV of a
+// key depend on its own chunk only; dQ sums the chunks in turn).  That bounds
+// the buffer for any block length, which keeps long blocks (a (b, h) slice of
+// 4 GiB or more) and smaller workspaces on the five-product path instead of
+// recomputing S and dP for dQ.  Chunks are whole dK/dV key tiles and at least
+// kMinDsChunk keys: shorter ones leave the dQ workgroups too little work.
+constexpr int64_t kMinDsChunk = 1024;
+// dS^T that the default workspace provides for a block whose whole dS^T does
+// not fit 4 GiB (b, h) slices: chunks of at most this many bytes in all.
+constexpr size_t kDefaultDsChunkBytes = (size_t)16 << 30;
+
+static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// dS^T bytes per key of a block with lq query rows, over all (b, h) slices.
+static int64_t ds_bytes_per_key(const ra_problem* p, int64_t lq) {
+  return (int64_t)p->batch * p->heads * ds_ld_of(lq) * 2;
+}
+
+// Keys per dS^T chunk of a block of lq rows x lk keys with `avail` bytes for
+// dS^T: the whole (tile-padded) block when it fits, else the largest multiple
+// of the key tile that fits and keeps one (b, h) slice under 4 GiB; 0 (dQ
+// recomputes S and dP) when that is under kMinDsChunk keys, and for fp32.
+static int64_t ds_chunk_keys(const ra_problem* p, int64_t lq, int64_t lk, size_t avail) {
+  if (p->dtype != RA_DTYPE_BF16 || lq == 0 || lk == 0) return 0;
+  const int64_t full = round_up(lk, BWD_BK);
+  const int64_t slice_cap = ((((int64_t)1 << 32) - 1) / (ds_ld_of(lq) * 2)) / BWD_BK * BWD_BK;
+  int64_t kc = std::min<int64_t>((int64_t)(avail / (size_t)ds_bytes_per_key(p, lq)), slice_cap);
+  kc = kc / BWD_BK * BWD_BK;
+  if (kc >= full) return full;
+  return kc >= kMinDsChunk ? kc : 0;
+}
+
+// dS^T bytes of the default workspace for one block: the whole block when its
+// (b, h) slices stay under 4 GiB, else chunks within kDefaultDsChunkBytes.
+static size_t ds_default_bytes(const ra_problem* p, int64_t lq, int64_t lk) {
+  if (p->dtype != RA_DTYPE_BF16 || lq == 0 || lk == 0) return 0;
+  const int64_t full = round_up(lk, BWD_BK);
+  if (full * ds_ld_of(lq) * 2 < ((int64_t)1 << 32)) return (size_t)(full * ds_bytes_per_key(p, lq));
+  return (size_t)(ds_chunk_keys(p, lq, lk, kDefaultDsChunkBytes) * ds_bytes_per_key(p, lq));
+}
+
+// Local indices [c0, c0 + n) of a posmap as a posmap of their own.
+static ra_posmap sub_posmap(const ra_posmap& m, int64_t c0, int64_t n) {
+  ra_posmap r{};
+  int64_t base = 0;
+  for (int i = 0; i < m.nseg; ++i) {
+    const ra_seg& g = m.seg[i];
+    const int64_t lo = std::max(c0, base), hi = std::min(c0 + n, base + g.len);
+    if (lo < hi) r.seg[r.nseg++] = ra_seg{g.begin + (lo - base) * g.stride, g.stride, hi - lo};
+    base += g.len;
+  }
+  if (r.nseg == 0) r = ra_posmap{1, {ra_seg{0, 1, 0}, ra_seg{0, 1, 0}}};
+  return r;
+}
+
+// dS^T bytes of the stored-dS path in the default workspace: one piece's (in
+// chunks when its slices would reach 4 GiB), or every piece's side by side for
+// the grouped launches of a per-sequence layout (bf16; fp32 stores none).
 static size_t ds_bytes_ring(const std::vector<Piece>& pieces) {
-  return pieces.size() > 1 ? ds_bytes_sum(pieces) : ds_bytes_max(pieces);
+  if (pieces.size() > 1) return ds_bytes_sum(pieces);
+  return pieces.empty() ? 0 : ds_default_bytes(&pieces[0].prob, pieces[0].L, pieces[0].L);
 }
 
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world) {
@@ -972,10 +1021,20 @@ static ra_status ring_bwd_impl(const ra_problem* prob, ra_layout layout, int32_t
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
            "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-  // The dS^T buffer when the workspace holds it, else none (then dQ comes from
-  // the recompute kernel).
-  const size_t dsb = ds_bytes_ring(pieces);
-  uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
+  // The dS^T buffer when the workspace holds it (one piece: in chunks of kc
+  // keys when it holds less than the whole block), else none (then dQ comes
+  // from the recompute kernel).
+  uint16_t* const ds_buf = (uint16_t*)((char*)workspace + need);
+  const size_t avail = workspace_bytes - need;
+  int64_t kc = 0;
+  uint16_t* dsT = nullptr;
+  if (pieces.size() == 1) {
+    kc = ds_chunk_keys(&pieces[0].prob, pieces[0].L, pieces[0].L, avail);
+    dsT = kc > 0 ? ds_buf : nullptr;
+  } else {
+    const size_t dsb = ds_bytes_sum(pieces);
+    dsT = (dsb > 0 && avail >= dsb) ? ds_buf : nullptr;
+  }
 
   float* delta = (float*)workspace;
   hipStream_t s = (hipStream_t)stream;
@@ -1039,7 +1098,7 @@ static ra_status ring_bwd_impl(const ra_problem* prob, ra_layout layout, int32_t
     where = assign_pieces(pieces, ns);
     if ((st = fork_streams(pool, ns, s)) != RA_OK) return st;
   }
-  auto run_piece = [&](const Piece& pc, hipStream_t ps, uint16_t* dsT) -> ra_status {
+  auto run_piece = [&](const Piece& pc, hipStream_t ps, uint16_t* dsT, int64_t kc) -> ra_status {
     const ra_problem* pp = &pc.prob;
     const ra_tensor qp = shift_rows(q_local, pc.row0, esz), kp = shift_rows(k_ring, pc.row0, esz);
     const ra_tensor vp = shift_rows(v_ring, pc.row0, esz), dop = shift_rows(dout, pc.row0, esz);
@@ -1052,25 +1111,33 @@ static ra_status ring_bwd_impl(const ra_problem* prob, ra_layout layout, int32_t
       ra_posmap kmap;
       make_posmap(lay, pp->seq_len, world, src, &kmap);
       if (!step_has_pairs(pp, qmap, pc.L, kmap, pc.L)) continue;
-      BwdArgs a;
-      bwd_args(pp, qp, pc.L, qmap, offset_rd(kp, src * stride_rank, esz), offset_rd(vp, src * stride_rank, esz),
-               pc.L, kmap, dop, lse + pc.row0, delta + pc.row0, wr(dqp), offset_wr(dkp, src * stride_rank_grad, 4),
-               offset_wr(dvp, src * stride_rank_grad, 4), &a);
-      a.lse_sh = L;
-      a.dsT = dsT;
-      a.ds_ld = ds_ld_of(pc.L);
-      ra_status st2 = launch_bwd_step(a, pp->head_dim, bf16, step, ps);
-      if (st2 != RA_OK) return st2;
+      // the step's keys in chunks of kc (one chunk without a dS^T buffer)
+      const int64_t ck = (dsT && kc > 0) ? kc : pc.L;
+      for (int64_t c0 = 0; c0 < pc.L; c0 += ck) {
+        const int64_t n = std::min(ck, pc.L - c0);
+        const ra_posmap km = n == pc.L ? kmap : sub_posmap(kmap, c0, n);
+        if (!step_has_pairs(pp, qmap, pc.L, km, n)) continue;
+        BwdArgs a;
+        bwd_args(pp, qp, pc.L, qmap, offset_rd(shift_rows(kp, c0, esz), src * stride_rank, esz),
+                 offset_rd(shift_rows(vp, c0, esz), src * stride_rank, esz), n, km, dop, lse + pc.row0,
+                 delta + pc.row0, wr(dqp), offset_wr(shift_rows(dkp, c0, 4), src * stride_rank_grad, 4),
+                 offset_wr(shift_rows(dvp, c0, 4), src * stride_rank_grad, 4), &a);
+        a.lse_sh = L;
+        a.dsT = dsT;
+        a.ds_ld = ds_ld_of(pc.L);
+        ra_status st2 = launch_bwd_step(a, pp->head_dim, bf16, step, ps);
+        if (st2 != RA_OK) return st2;
+      }
     }
     return RA_OK;
   };
-  if (pieces.size() == 1) return run_piece(pieces[0], s, dsT);
+  if (pieces.size() == 1) return run_piece(pieces[0], s, dsT, kc);
   if (ns == 1) {
-    for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i) st = run_piece(pieces[i], s, nullptr);
+    for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i) st = run_piece(pieces[i], s, nullptr, 0);
     return st;
   }
   for (size_t i = 0; i < pieces.size() && st == RA_OK; ++i)
-    st = run_piece(pieces[i], pool->st[where[i]], nullptr);
+    st = run_piece(pieces[i], pool->st[where[i]], nullptr, 0);
   const ra_status sj = join_streams(pool, ns, s);
   return st != RA_OK ? st : sj;
 }
@@ -1150,10 +1217,7 @@ static ra_status gathered_common(const ra_problem* prob, ra_layout layout, int32
 // dS^T bytes of a gathered share: b*h slices of round_up(nk, 128) keys x round_up(L, 128)
 // rows (bf16), 0 when not applicable (fp32, or a slice beyond 32-bit byte offsets).
 static size_t gathered_ds_bytes(const ra_problem* prob, int64_t L, int64_t nk) {
-  if (prob->dtype != RA_DTYPE_BF16 || L == 0 || nk <= 0) return 0;
-  const int64_t slice = (nk + BWD_BK - 1) / BWD_BK * BWD_BK * ds_ld_of(L) * 2;
-  if (slice >= ((int64_t)1 << 32)) return 0;
-  return (size_t)prob->batch * prob->heads * (size_t)slice;
+  return nk > 0 ? ds_default_bytes(prob, L, nk) : 0;
 }
 
 size_t ra_gathered_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank) {
@@ -1235,8 +1299,9 @@ ra_status ra_gathered_bwd(const ra_problem* prob, ra_layout layout, int32_t worl
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,
            "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   RA_CHECK(((uintptr_t)workspace & 15) == 0, RA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-  const size_t dsb = gathered_ds_bytes(prob, L, nk);
-  uint16_t* dsT = (dsb > 0 && workspace_bytes >= need + dsb) ? (uint16_t*)((char*)workspace + need) : nullptr;
+  // dS^T in chunks of kc keys when the workspace holds less than the whole block
+  const int64_t kc = ds_chunk_keys(prob, L, nk, workspace_bytes - need);
+  uint16_t* dsT = kc > 0 ? (uint16_t*)((char*)workspace + need) : nullptr;
   float* delta = (float*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = prob->dtype == RA_DTYPE_BF16;
@@ -1254,13 +1319,20 @@ ra_status ra_gathered_bwd(const ra_problem* prob, ra_layout layout, int32_t worl
   RA_HIP(timed(K_ZERO, -1, s, [&] {
     return launch_zero(dqw, prob->batch, prob->heads, (int32_t)L, prob->head_dim, s);
   }));
-  const ra_posmap kmap{1, {ra_seg{k_lo, 1, nk}, ra_seg{0, 1, 0}}};
-  BwdArgs a;
-  bwd_args(prob, q_local, L, qmap, rd(shift_rows(k_all, k_lo, esz)), rd(shift_rows(v_all, k_lo, esz)), nk, kmap,
-           dout, lse, delta, dqw, wr(shift_rows(dk_all, k_lo, 4)), wr(shift_rows(dv_all, k_lo, 4)), &a);
-  a.dsT = dsT;
-  a.ds_ld = ds_ld_of(L);
-  return launch_bwd_step(a, prob->head_dim, bf16, 0, s);
+  // the visible keys [k_lo, k_lo + nk) in chunks of kc (one chunk without a dS^T buffer)
+  const int64_t ck = dsT ? kc : nk;
+  for (int64_t c0 = 0; c0 < nk; c0 += ck) {
+    const int64_t n = std::min(ck, nk - c0), k0 = k_lo + c0;
+    const ra_posmap kmap{1, {ra_seg{k0, 1, n}, ra_seg{0, 1, 0}}};
+    if (n < nk && !step_has_pairs(prob, qmap, L, kmap, n)) continue;
+    BwdArgs a;
+    bwd_args(prob, q_local, L, qmap, rd(shift_rows(k_all, k0, esz)), rd(shift_rows(v_all, k0, esz)), n, kmap, dout,
+             lse, delta, dqw, wr(shift_rows(dk_all, k0, 4)), wr(shift_rows(dv_all, k0, 4)), &a);
+    a.dsT = dsT;
+    a.ds_ld = ds_ld_of(L);
+    if ((st = launch_bwd_step(a, prob->head_dim, bf16, 0, s)) != RA_OK) return st;
+  }
+  return RA_OK;
 }
 
 }  // extern "C"

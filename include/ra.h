@@ -190,12 +190,15 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
  *  every rank into the same buffers yields the full gradients.
  *  workspace: device memory, 16-byte aligned, of at least ra_ring_workspace_min_bytes()
  *  bytes.  It holds delta = rowsum(dO * O) (the row term of the textbook softmax-attention
- *  gradient; the pages give no backward) and, for bf16 when it
- *  reaches ra_ring_workspace_bytes(), the bf16 dS^T of the current step: the dK/dV
- *  kernel then stores dS and dQ = dS K is one product per pair instead of a recompute
- *  of S, P and dP.  With less than that, dQ is computed by the recompute kernel.
+ *  gradient; the pages give no backward) and, for bf16, the bf16 dS^T of the current step
+ *  when the rest of the workspace holds it: the dK/dV kernel then stores dS and dQ = dS K
+ *  is one product per pair instead of a recompute of S, P and dP.  When the rest holds
+ *  the dS^T of only part of a step's keys (at least 1024 keys, in whole 128-key tiles),
+ *  each step runs in chunks of keys: the dK/dV kernel and the dQ-from-dS kernel once per
+ *  chunk (dK/dV are the same bit for bit; dQ adds the chunks in turn, so it agrees to
+ *  fp32 rounding).  With less than that, dQ is computed by the recompute kernel.
  *  The per-sequence layouts run their sequences as ra_ring_fwd does (bf16: grouped
- *  launches, every sequence with its own dS^T region side by side). */
+ *  launches, every sequence with its own dS^T region side by side; no chunks). */
 ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
                       ra_tensor q_local, ra_tensor k_ring, ra_tensor v_ring, int64_t stride_rank,
                       ra_tensor out, const float* lse, ra_tensor dout,
@@ -223,9 +226,12 @@ ra_status ra_ring_bwd_noalloc(const ra_problem* prob, ra_layout layout, int32_t 
 size_t ra_noalloc_scratch_bytes(void);
 
 /* Bytes of device workspace for ra_ring_bwd's fastest path (0 on invalid input):
- * delta (b*h*L fp32) and, for bf16, dS^T (b*h*round_up(L, 128)^2 bf16), L = S/N;
- * for a per-sequence layout, the sum of that dS^T size over the sequences, each
- * with its own local length in place of L.
+ * delta (b*h*L fp32) and, for bf16, dS^T (b*h*round_up(L, 128)^2 bf16), L = S/N.  When
+ * one (batch, head) slice of that dS^T would reach 4 GiB (what a buffer descriptor
+ * addresses; L above 46340), the dS^T of a chunk of keys instead: the most whole
+ * 128-key tiles that keep a slice below 4 GiB and all slices within 16 GiB (the
+ * backward then runs each step in chunks, see ra_ring_bwd).  For a per-sequence layout,
+ * the sum of the whole dS^T size over the sequences, each with its own local length.
  * Never smaller than ra_ring_workspace_min_bytes(). */
 size_t ra_ring_workspace_bytes(const ra_problem* prob, ra_layout layout, int32_t world);
 
@@ -257,8 +263,8 @@ ra_status ra_gathered_fwd(const ra_problem* prob, ra_layout layout, int32_t worl
  * keys the share sees, so that running every rank into the same buffers gives the full
  * gradients (a reduce-scatter on a real ring).  Workspace as for ra_ring_bwd: at least
  * ra_gathered_workspace_min_bytes() (delta; dQ then recomputes S and dP), or
- * ra_gathered_workspace_bytes() for the stored-dS path (bf16 only, and only when one
- * (batch, head) slice of dS^T stays below 4 GiB). */
+ * ra_gathered_workspace_bytes() for the stored-dS path (bf16 only; the visible keys in
+ * chunks when the workspace, or a 4 GiB (batch, head) slice, holds only part of them). */
 ra_status ra_gathered_bwd(const ra_problem* prob, ra_layout layout, int32_t world, int32_t rank,
                           ra_tensor q_local, ra_tensor k_all, ra_tensor v_all,
                           ra_tensor out, const float* lse, ra_tensor dout,
