@@ -108,7 +108,10 @@ ra_status check_problem(const ra_problem* p) {
 
 size_t elem_size(ra_dtype d) { return d == RA_DTYPE_BF16 ? 2 : 4; }
 
-ra_status check_tensor(const char* name, const ra_tensor& t, size_t esz, int64_t rows, bool need) {
+// Results and accumulators (out, dQ, dK, dV and their bf16 copies): the kernels
+// address them with 64-bit pointer arithmetic, so their slices may be of any
+// size.
+ra_status check_out_tensor(const char* name, const ra_tensor& t, size_t esz, bool need) {
   if (!need) return RA_OK;
   RA_CHECK(t.ptr != nullptr, RA_ERR_INVALID_ARG, "%s: NULL pointer", name);
   RA_CHECK(((uintptr_t)t.ptr & 15) == 0, RA_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", name);
@@ -116,7 +119,15 @@ ra_status check_tensor(const char* name, const ra_tensor& t, size_t esz, int64_t
   const int64_t b16 = 16 / (int64_t)esz;  // elements per 16 bytes
   RA_CHECK(t.stride_b % b16 == 0 && t.stride_t % b16 == 0 && t.stride_h % b16 == 0, RA_ERR_INVALID_ARG,
            "%s: strides must keep rows 16-byte aligned", name);
-  // Kernels address one (batch, head) slice with 32-bit byte offsets and read
+  return RA_OK;
+}
+
+// Operands the kernels read through buffer descriptors (q, k, v, dout).
+ra_status check_tensor(const char* name, const ra_tensor& t, size_t esz, int64_t rows, bool need) {
+  if (!need) return RA_OK;
+  ra_status st = check_out_tensor(name, t, esz, need);
+  if (st != RA_OK) return st;
+  // One (batch, head) slice is addressed with 32-bit byte offsets, and reads go
   // up to 256 rows past its end (those reads return zeros).
   RA_CHECK((rows + 256) * t.stride_t * (int64_t)esz + 512 * (int64_t)esz < (int64_t(1) << 31), RA_ERR_UNSUPPORTED,
            "%s: a (batch, head) slice spans more than 2 GiB", name);
@@ -416,7 +427,7 @@ ra_status ra_block_attn_fwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_
   if ((st = check_tensor("q", q, esz, lq, true)) != RA_OK) return st;
   if ((st = check_tensor("k", k, esz, lk, lk > 0)) != RA_OK) return st;
   if ((st = check_tensor("v", v, esz, lk, lk > 0)) != RA_OK) return st;
-  if ((st = check_tensor("out_b", out_b, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out_b", out_b, 4, true)) != RA_OK) return st;
   if ((st = check_ptr("lse_b", lse_b)) != RA_OK) return st;
   if ((st = check_posmap("qmap", qmap, lq, prob->seq_len)) != RA_OK) return st;
   if (lk > 0 && (st = check_posmap("kmap", kmap, lk, prob->seq_len)) != RA_OK) return st;
@@ -451,8 +462,8 @@ ra_status ra_lse_merge(const ra_problem* prob, int64_t lq, ra_tensor out, float*
   if (st != RA_OK) return st;
   RA_CHECK(lq >= 0 && lq <= kMaxPos, RA_ERR_INVALID_ARG, "lq out of range");
   if (lq == 0) return RA_OK;
-  if ((st = check_tensor("out", out, 4, lq, true)) != RA_OK) return st;
-  if ((st = check_tensor("out_b", out_b, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out", out, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out_b", out_b, 4, true)) != RA_OK) return st;
   if ((st = check_ptr("lse", lse)) != RA_OK) return st;
   if ((st = check_ptr("lse_b", lse_b)) != RA_OK) return st;
   MergeArgs a{};
@@ -475,7 +486,7 @@ ra_status ra_bwd_preprocess(const ra_problem* prob, int64_t lq, ra_tensor out, r
   if (st != RA_OK) return st;
   RA_CHECK(lq >= 0 && lq <= kMaxPos, RA_ERR_INVALID_ARG, "lq out of range");
   if (lq == 0) return RA_OK;
-  if ((st = check_tensor("out", out, 4, lq, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out", out, 4, true)) != RA_OK) return st;
   if ((st = check_tensor("dout", dout, elem_size(prob->dtype), lq, true)) != RA_OK) return st;
   if ((st = check_ptr("delta", delta)) != RA_OK) return st;
   PrepArgs a{};
@@ -548,9 +559,9 @@ ra_status ra_block_attn_bwd(const ra_problem* prob, ra_tensor q, int64_t lq, ra_
   if ((st = check_tensor("k", k, esz, lk, true)) != RA_OK) return st;
   if ((st = check_tensor("v", v, esz, lk, true)) != RA_OK) return st;
   if ((st = check_tensor("dout", dout, esz, lq, true)) != RA_OK) return st;
-  if ((st = check_tensor("dq_acc", dq_acc, 4, lq, true)) != RA_OK) return st;
-  if ((st = check_tensor("dk_acc", dk_acc, 4, lk, true)) != RA_OK) return st;
-  if ((st = check_tensor("dv_acc", dv_acc, 4, lk, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dq_acc", dq_acc, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dk_acc", dk_acc, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dv_acc", dv_acc, 4, true)) != RA_OK) return st;
   if ((st = check_ptr("lse", lse)) != RA_OK) return st;
   if ((st = check_ptr("delta", delta)) != RA_OK) return st;
   if ((st = check_posmap("qmap", qmap, lq, prob->seq_len)) != RA_OK) return st;
@@ -853,8 +864,8 @@ ra_status ra_ring_fwd(const ra_problem* prob, ra_layout layout, int32_t world, i
   if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
   if ((st = check_tensor("k_ring", k_ring, esz, L, true)) != RA_OK) return st;
   if ((st = check_tensor("v_ring", v_ring, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("out_lowp", out_lowp, esz, L, out_lowp.ptr != nullptr)) != RA_OK) return st;
+  if ((st = check_out_tensor("out", out, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out_lowp", out_lowp, esz, out_lowp.ptr != nullptr)) != RA_OK) return st;
   if ((st = check_ptr("lse", lse)) != RA_OK) return st;
   RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
            "stride_rank must be >= 0 and keep 16-byte alignment");
@@ -1007,11 +1018,11 @@ static ra_status ring_bwd_impl(const ra_problem* prob, ra_layout layout, int32_t
   if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
   if ((st = check_tensor("k_ring", k_ring, esz, L, true)) != RA_OK) return st;
   if ((st = check_tensor("v_ring", v_ring, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out", out, 4, true)) != RA_OK) return st;
   if ((st = check_tensor("dout", dout, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("dq", dq, 4, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("dk_ring", dk_ring, 4, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("dv_ring", dv_ring, 4, L, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dq", dq, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dk_ring", dk_ring, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dv_ring", dv_ring, 4, true)) != RA_OK) return st;
   if ((st = check_ptr("lse", lse)) != RA_OK) return st;
   RA_CHECK(stride_rank >= 0 && stride_rank % (int64_t)(16 / esz) == 0, RA_ERR_INVALID_ARG,
            "stride_rank must be >= 0 and keep 16-byte alignment");
@@ -1248,8 +1259,8 @@ ra_status ra_gathered_fwd(const ra_problem* prob, ra_layout layout, int32_t worl
   if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
   if ((st = check_tensor("k_all", shift_rows(k_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
   if ((st = check_tensor("v_all", shift_rows(v_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
-  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("out_lowp", out_lowp, esz, L, out_lowp.ptr != nullptr)) != RA_OK) return st;
+  if ((st = check_out_tensor("out", out, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out_lowp", out_lowp, esz, out_lowp.ptr != nullptr)) != RA_OK) return st;
   if ((st = check_ptr("lse", lse)) != RA_OK) return st;
   const ra_posmap kmap{1, {ra_seg{k_lo, 1, nk}, ra_seg{0, 1, 0}}};
   FwdArgs a{};
@@ -1289,11 +1300,11 @@ ra_status ra_gathered_bwd(const ra_problem* prob, ra_layout layout, int32_t worl
   if ((st = check_tensor("q_local", q_local, esz, L, true)) != RA_OK) return st;
   if ((st = check_tensor("k_all", shift_rows(k_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
   if ((st = check_tensor("v_all", shift_rows(v_all, k_lo, esz), esz, nk, true)) != RA_OK) return st;
-  if ((st = check_tensor("out", out, 4, L, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("out", out, 4, true)) != RA_OK) return st;
   if ((st = check_tensor("dout", dout, esz, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("dq", dq, 4, L, true)) != RA_OK) return st;
-  if ((st = check_tensor("dk_all", shift_rows(dk_all, k_lo, 4), 4, nk, true)) != RA_OK) return st;
-  if ((st = check_tensor("dv_all", shift_rows(dv_all, k_lo, 4), 4, nk, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dq", dq, 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dk_all", shift_rows(dk_all, k_lo, 4), 4, true)) != RA_OK) return st;
+  if ((st = check_out_tensor("dv_all", shift_rows(dv_all, k_lo, 4), 4, true)) != RA_OK) return st;
   if ((st = check_ptr("lse", lse)) != RA_OK) return st;
   const size_t need = ra_gathered_workspace_min_bytes(prob, layout, world, rank);
   RA_CHECK(workspace != nullptr && workspace_bytes >= need, RA_ERR_WORKSPACE,

@@ -97,7 +97,11 @@ typedef struct { int64_t begin, stride, len; } ra_seg;
 typedef struct { int32_t nseg; ra_seg seg[2]; } ra_posmap;
 
 /* A token-major tensor: element (b, t, h, d) lives at
- * ptr + b*stride_b + t*stride_t + h*stride_h + d (in elements). */
+ * ptr + b*stride_b + t*stride_t + h*stride_h + d (in elements).  Pointer and strides
+ * keep every row 16-byte aligned.  The operands read through buffer descriptors
+ * (q, k, v, dout) must have (batch, head) slices below 2 GiB counting 256 rows past
+ * the last one (RA_ERR_UNSUPPORTED otherwise: 32-bit offsets); results and
+ * accumulators (out, dq, dk, dv and the bf16 copies) have no size limit. */
 typedef struct { void* ptr; int64_t stride_b, stride_t, stride_h; } ra_tensor;
 
 typedef struct {

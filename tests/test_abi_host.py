@@ -228,3 +228,18 @@ def test_default_workspace_chunks_long_blocks(ra):
     kc = ((2 ** 32 - 1) // (262144 * 2)) // 128 * 128
     assert kc == 8064
     assert lib.ra_ring_workspace_bytes(C.byref(p), 0, 8) == need + kc * 2 * 262144 * 2
+
+
+def test_slice_limit_applies_to_descriptor_operands_only(ra):
+    """q/k/v/dout are read through buffer descriptors (32-bit offsets): a (batch,
+    head) slice of 2 GiB or more is RA_ERR_UNSUPPORTED.  Results and accumulators
+    are written through 64-bit addresses: the same slice passes their check (the
+    call then stops at the next argument, a NULL lse)."""
+    from exact_long_context_ra_amd._lib import RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED
+    lib = ra.lib()
+    huge = _t(st=1 << 24, sh=64)   # 32 MiB per row (bf16): 16 rows + the 256-row overrun pass 2 GiB
+    assert _ring_fwd(ra, _problem(ra), q=huge) == RA_ERR_UNSUPPORTED
+    assert b"q_local" in lib.ra_last_error()
+    huge_out = _t(st=1 << 23, sh=64)  # 32 MiB per row (fp32)
+    assert _ring_fwd(ra, _problem(ra), out=huge_out, lse=None) == RA_ERR_INVALID_ARG
+    assert b"lse" in lib.ra_last_error()
