@@ -55,7 +55,7 @@ WORKLOADS = {
     "zigzag_varlen": ("zigzag_varlen", 131072, 8, [0], True, False),
     "stripe_varlen": ("stripe_varlen", 131072, 8, [0], True, False),
     # a long context: one million tokens on 8 ranks, rank 0's zigzag share (131072
-    # rows; its dS^T goes through the backward in key chunks within 16 GiB)
+    # rows; its dS^T goes through the backward in key chunks within 32 GiB)
     "zigzag_1m": ("zigzag", 1048576, 8, [0], False, False),
 }
 DEFAULT_ALSO = "stripe,contiguous,varlen,varlen_gathered,zigzag_varlen,stripe_varlen,zigzag_1m"

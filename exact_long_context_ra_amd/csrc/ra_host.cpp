@@ -938,7 +938,7 @@ size_t ra_ring_workspace_min_bytes(const ra_problem* prob, ra_layout layout, int
 constexpr int64_t kMinDsChunk = 1024;
 // dS^T that the default workspace provides for a block whose whole dS^T does
 // not fit 4 GiB (b, h) slices: chunks of at most this many bytes in all.
-constexpr size_t kDefaultDsChunkBytes = (size_t)16 << 30;
+constexpr size_t kDefaultDsChunkBytes = (size_t)32 << 30;
 
 static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 

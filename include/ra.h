@@ -233,7 +233,7 @@ size_t ra_noalloc_scratch_bytes(void);
  * delta (b*h*L fp32) and, for bf16, dS^T (b*h*round_up(L, 128)^2 bf16), L = S/N.  When
  * one (batch, head) slice of that dS^T would reach 4 GiB (what a buffer descriptor
  * addresses; L above 46340), the dS^T of a chunk of keys instead: the most whole
- * 128-key tiles that keep a slice below 4 GiB and all slices within 16 GiB (the
+ * 128-key tiles that keep a slice below 4 GiB and all slices within 32 GiB (the
  * backward then runs each step in chunks, see ra_ring_bwd).  For a per-sequence layout,
  * the sum of the whole dS^T size over the sequences, each with its own local length.
  * Never smaller than ra_ring_workspace_min_bytes(). */

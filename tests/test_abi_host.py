@@ -211,17 +211,17 @@ def test_noalloc_rejects_before_any_gpu_call(ra):
 def test_default_workspace_chunks_long_blocks(ra):
     """Default backward workspace: the whole block's dS^T while each (b, h) slice
     stays under the 4 GiB a buffer descriptor addresses; beyond, dS^T chunks of
-    whole 128-key tiles within 16 GiB (host arithmetic, no GPU)."""
+    whole 128-key tiles within 32 GiB (host arithmetic, no GPU)."""
     lib = ra.lib()
     # zigzag, 32 heads, 8 ranks: S/N = 32768 -> slice 32768^2 * 2 B = 2 GiB (whole block)
     p = _problem(ra, heads=32, head_dim=128, seq_len=8 * 32768)
     need = lib.ra_ring_workspace_min_bytes(C.byref(p), 1, 8)
     assert need == 32 * 32768 * 4
     assert lib.ra_ring_workspace_bytes(C.byref(p), 1, 8) == need + 32 * 32768 * 32768 * 2
-    # S/N = 65536 -> slice 8 GiB: chunks of 16 GiB / (32 * 65536 * 2 B per key) = 4096 keys
+    # S/N = 65536 -> slice 8 GiB: chunks of 32 GiB / (32 * 65536 * 2 B per key) = 8192 keys
     p = _problem(ra, heads=32, head_dim=128, seq_len=8 * 65536)
     need = lib.ra_ring_workspace_min_bytes(C.byref(p), 1, 8)
-    assert lib.ra_ring_workspace_bytes(C.byref(p), 1, 8) == need + 4096 * 32 * 65536 * 2
+    assert lib.ra_ring_workspace_bytes(C.byref(p), 1, 8) == need + 8192 * 32 * 65536 * 2
     # S/N = 262144, 2 heads -> 1 MiB per key, but a slice must stay under 4 GiB: 8064 keys
     p = _problem(ra, heads=2, head_dim=128, seq_len=8 * 262144)
     need = lib.ra_ring_workspace_min_bytes(C.byref(p), 0, 8)
