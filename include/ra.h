@@ -217,8 +217,9 @@ ra_status ra_ring_bwd(const ra_problem* prob, ra_layout layout, int32_t world, i
  * nothing, and nothing in the scratch needs clearing between calls (every value read is
  * written earlier in the same call).  A problem whose delta (4 * batch * heads * S/N bytes,
  * rounded up to 256) exceeds the array is rejected with RA_ERR_WORKSPACE before anything
- * is enqueued; when delta fits but the dS^T does not, dQ comes from the recompute kernel
- * (ra_ring_bwd's minimal-workspace path).  The fp32 per-sequence layouts run their
+ * is enqueued; when delta fits, the rest of the array takes the dS^T as ra_ring_bwd's
+ * workspace would (whole steps, or chunks of at least 1024 keys), and with room for
+ * less than that dQ comes from the recompute kernel (the minimal-workspace path).  The fp32 per-sequence layouts run their
  * sequences one after another on `stream` (no side streams).  Every call on a GPU uses
  * that GPU's one array: calls that may overlap on one GPU (other streams or threads)
  * race and must be serialised by the caller.  Other arguments and results as ra_ring_bwd. */
