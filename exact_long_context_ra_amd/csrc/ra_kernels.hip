@@ -1631,7 +1631,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
     // query tile qt from `buf`/`lbuf` while tile qt + 1 is fetched into `nbuf`/`nlbuf`
     auto step = [&](int qt, const char* buf, const char* lbuf, char* nbuf, char* nlbuf) {
       flush();
-      if (qt + 1 <= qt1) issue(qt + 1, nbuf, nlbuf);
       const char* sQ = buf;
       const char* sDO = buf + C::OFF_DO;
       const float* sLse = reinterpret_cast<const float*>(lbuf);
@@ -1646,13 +1645,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
         wave_empty = qlast < cbf.lo || qfirst > cbl.hi;
         wave_full = (kw0 + 32 <= a.lk) && (rw0 + 32 <= a.lq) && qfirst >= cbl.lo && qlast <= cbf.hi;
       }
+      // S = Q K^T and dP = dO V^T, the two chains interleaved with S half of
+      // its k-steps ahead, so that S is complete while the last dP products
+      // run.
+      const int hr0 = qh * 32;
+      constexpr int LEAD = D / 32;
+      f32x16 s = f32x16{}, dp = f32x16{};
       if (!wave_empty) {
-        const int hr0 = qh * 32;
-        // S = Q K^T and dP = dO V^T, the two chains interleaved with S half
-        // of its k-steps ahead, so that S is complete while the last dP
-        // products run.
-        constexpr int LEAD = D / 32;
-        f32x16 s = f32x16{}, dp = f32x16{};
         const int qrow = hr0 + row_perm(l32);
 #pragma unroll
         for (int c = 0; c < D / 16 + LEAD; ++c) {
@@ -1670,6 +1669,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      // The next query tile is copied in from here, not from the start of the
+      // step: its copies then stay out of the S/dP products' operand reads,
+      // and half a step is still time enough for them to land.
+      if (qt + 1 <= qt1) issue(qt + 1, nbuf, nlbuf);
+      if (!wave_empty) {
         // lse (natural log, taken to base 2 in the exponent) and delta of this
         // lane's 16 rows (rows hr0 + 16u + 8hf + i2 for half u) come as two
         // 16-byte reads each.
