@@ -791,6 +791,18 @@ static std::vector<PiecePlan> plan_pieces(const std::vector<Piece>& pieces, ra_l
   return plans;
 }
 
+// First local query row of a piece, rounded down to a multiple of 16, from
+// which its rows can see a key of this step's block: under the causal mask a
+// row sees nothing before the block's first key position, and positions grow
+// with the row.  The forward and dQ launches start there (a per-sequence
+// zigzag ring's first chunk sees no key after step 0, so its rows would
+// otherwise fill, and straddle, whole row tiles for nothing).
+static int32_t first_seeing_row(const Piece& pc, const ra_posmap& qmap, const ra_posmap& kmap) {
+  if (!pc.prob.causal || pc.prob.num_seqs > 0 || pc.L == 0) return 0;
+  const int64_t qa = std::min<int64_t>(h_first_ge(qmap, pos_at(kmap, 0)), pc.L - 1);
+  return (int32_t)(qa / 16 * 16);
+}
+
 // The pieces active at `step`, longest first, in groups of at most kMaxPieces.
 // Workgroups are dispatched roughly in id order and a longer piece has the
 // longer-running workgroups, so putting it first keeps them off the end of the
@@ -841,8 +853,11 @@ static ra_status ring_fwd_grouped(const std::vector<Piece>& pieces, ra_layout la
         const int i = grp[j];
         a.g.row0[j] = (int32_t)pieces[i].row0;
         a.g.len[j] = (int32_t)pieces[i].L;
-        a.g.flags[j] = (step != plans[i].first ? PIECE_MERGE : 0) |
-                       (step == plans[i].last && out_lowp.ptr ? PIECE_LOWP : 0);
+        const bool merge = step != plans[i].first, lowp = step == plans[i].last && out_lowp.ptr;
+        a.g.flags[j] = (merge ? PIECE_MERGE : 0) | (lowp ? PIECE_LOWP : 0);
+        // rows that see no key are left out only where a merge leaves them as
+        // they are (not on the step that first stores them or writes the copy)
+        a.g.qoff[j] = merge && !lowp ? first_seeing_row(pieces[i], plans[i].qmap, plans[i].kmap[step]) : 0;
         a.g.qmap[j] = to_dmap(plans[i].qmap);
         a.g.kmap[j] = to_dmap(plans[i].kmap[step]);
       }
@@ -1093,6 +1108,7 @@ static ra_status ring_bwd_impl(const ra_problem* prob, ra_layout layout, int32_t
           a.g.kmap[j] = to_dmap(plans[i].kmap[step]);
           a.g.ds_off[j] = ds_off[i];
           a.g.ds_ld[j] = ds_ld_of(pieces[i].L);
+          a.g.qoff[j] = first_seeing_row(pieces[i], plans[i].qmap, plans[i].kmap[step]);  // dQ launch only
         }
         if ((st = launch_bwd_step(a, p0->head_dim, true, step, s)) != RA_OK) return st;
       }

@@ -48,6 +48,10 @@ struct PieceTable {
   int32_t wg_begin[kMaxPieces + 1];
   int32_t row0[kMaxPieces], len[kMaxPieces];
   int32_t flags[kMaxPieces];  // forward: bit 0 merge into out/lse (else store), bit 1 write out_lowp
+  // Forward and dQ kernels: the first query row (within the piece, a multiple
+  // of 16) of the rows they process; the rows before it see no key at this
+  // step.  The dK/dV kernel always takes all of the piece's query rows.
+  int32_t qoff[kMaxPieces];
   DMap qmap[kMaxPieces], kmap[kMaxPieces];
   int64_t ds_off[kMaxPieces];  // backward: element offset of the piece's dS^T region
   int64_t ds_ld[kMaxPieces];
@@ -86,6 +90,7 @@ struct BwdArgs {
   // the dK/dV kernel when set; read by the dQ-from-dS kernel.
   uint16_t* dsT;
   int64_t ds_ld;
+  int32_t ds_row0;   // dQ-from-dS: dS^T row of this launch's query row 0 (a multiple of 16)
   PieceTable g;      // grouped launch (bf16 kernels only), g.n = 0 otherwise
 };
 

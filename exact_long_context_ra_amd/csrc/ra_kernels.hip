@@ -176,6 +176,23 @@ __device__ __forceinline__ int xcd_logical(int bid, int total) {
   return (bid & 7) * (total >> 3) + (bid >> 3);
 }
 
+// The posmap of local indices [n0, total) of m (0 <= n0 < total).
+__device__ __forceinline__ DMap dmap_tail(const DMap& m, int n0) {
+  DMap r = m;
+  if (n0 <= 0) return r;
+  if (n0 < m.s0.len) {
+    r.s0.begin += n0 * m.s0.stride;
+    r.s0.len -= n0;
+  } else {
+    const int k = n0 - m.s0.len;
+    r.nseg = 1;
+    r.s0 = DSeg{m.s1.begin + k * m.s1.stride, m.s1.stride, m.s1.len - k};
+    r.s1 = DSeg{0, 1, 0};
+  }
+  r.total = m.total - n0;
+  return r;
+}
+
 // Block of a grouped launch (a table of independent rings, see PieceTable):
 // finds this block's piece, points the row-based tensors at its rows and sets
 // its lengths, posmaps and flags; bid/nblk become the block index and count
@@ -191,41 +208,50 @@ __device__ __forceinline__ void fwd_piece(const FwdArgs& ap, FwdArgs& a, int& bi
   bid = (int)blockIdx.x - g.wg_begin[p];
   nblk = g.wg_begin[p + 1] - g.wg_begin[p];
   const int64_t r0 = g.row0[p];
+  const int qo = g.qoff[p];
+  const int64_t q0 = r0 + qo;  // first query row of this launch
   const int f = g.flags[p];
-  a.q.ptr = reinterpret_cast<const char*>(ap.q.ptr) + r0 * ap.q.st * 2;
+  a.q.ptr = reinterpret_cast<const char*>(ap.q.ptr) + q0 * ap.q.st * 2;
   a.k.ptr = reinterpret_cast<const char*>(ap.k.ptr) + r0 * ap.k.st * 2;
   a.v.ptr = reinterpret_cast<const char*>(ap.v.ptr) + r0 * ap.v.st * 2;
-  a.out.ptr = reinterpret_cast<char*>(ap.out.ptr) + r0 * ap.out.st * 4;
-  a.out_lowp.ptr = (f & PIECE_LOWP) ? reinterpret_cast<char*>(ap.out_lowp.ptr) + r0 * ap.out_lowp.st * 2 : nullptr;
-  a.lse = ap.lse + r0;
-  a.lq = a.lk = g.len[p];
-  a.qmap = g.qmap[p];
+  a.out.ptr = reinterpret_cast<char*>(ap.out.ptr) + q0 * ap.out.st * 4;
+  a.out_lowp.ptr = (f & PIECE_LOWP) ? reinterpret_cast<char*>(ap.out_lowp.ptr) + q0 * ap.out_lowp.st * 2 : nullptr;
+  a.lse = ap.lse + q0;
+  a.lq = g.len[p] - qo;
+  a.lk = g.len[p];
+  a.qmap = dmap_tail(g.qmap[p], qo);
   a.kmap = g.kmap[p];
   a.mode = (f & PIECE_MERGE) ? FWD_MERGE : FWD_STORE;
-  a.n_qtiles = (g.len[p] + FWD_BQ - 1) / FWD_BQ;
+  a.n_qtiles = (a.lq + FWD_BQ - 1) / FWD_BQ;
 }
-__device__ __forceinline__ void bwd_piece(const BwdArgs& ap, BwdArgs& a, int& bid, int& nblk) {
+// `qside`: the dQ kernels take the piece's query rows from qoff on; the dK/dV
+// kernel takes them all.
+__device__ __forceinline__ void bwd_piece(const BwdArgs& ap, BwdArgs& a, int& bid, int& nblk, bool qside) {
   const PieceTable& g = ap.g;
   const int p = piece_of(g, (int)blockIdx.x);
   bid = (int)blockIdx.x - g.wg_begin[p];
   nblk = g.wg_begin[p + 1] - g.wg_begin[p];
   const int64_t r0 = g.row0[p];
-  a.q.ptr = reinterpret_cast<const char*>(ap.q.ptr) + r0 * ap.q.st * 2;
+  const int qo = qside ? g.qoff[p] : 0;
+  const int64_t q0 = r0 + qo;  // first query row of this launch
+  a.q.ptr = reinterpret_cast<const char*>(ap.q.ptr) + q0 * ap.q.st * 2;
   a.k.ptr = reinterpret_cast<const char*>(ap.k.ptr) + r0 * ap.k.st * 2;
   a.v.ptr = reinterpret_cast<const char*>(ap.v.ptr) + r0 * ap.v.st * 2;
-  a.dout.ptr = reinterpret_cast<const char*>(ap.dout.ptr) + r0 * ap.dout.st * 2;
-  a.dq.ptr = reinterpret_cast<char*>(ap.dq.ptr) + r0 * ap.dq.st * 4;
+  a.dout.ptr = reinterpret_cast<const char*>(ap.dout.ptr) + q0 * ap.dout.st * 2;
+  a.dq.ptr = reinterpret_cast<char*>(ap.dq.ptr) + q0 * ap.dq.st * 4;
   a.dk.ptr = reinterpret_cast<char*>(ap.dk.ptr) + r0 * ap.dk.st * 4;
   a.dv.ptr = reinterpret_cast<char*>(ap.dv.ptr) + r0 * ap.dv.st * 4;
-  a.lse = ap.lse + r0;
-  a.delta = ap.delta + r0;
-  a.lq = a.lk = g.len[p];
-  a.qmap = g.qmap[p];
+  a.lse = ap.lse + q0;
+  a.delta = ap.delta + q0;
+  a.lq = g.len[p] - qo;
+  a.lk = g.len[p];
+  a.qmap = dmap_tail(g.qmap[p], qo);
   a.kmap = g.kmap[p];
-  a.n_ktiles = (g.len[p] + BWD_BK - 1) / BWD_BK;
-  a.n_qtiles = (g.len[p] + FWD_BQ - 1) / FWD_BQ;
+  a.n_ktiles = (a.lk + BWD_BK - 1) / BWD_BK;
+  a.n_qtiles = (a.lq + FWD_BQ - 1) / FWD_BQ;
   a.dsT = ap.dsT ? ap.dsT + g.ds_off[p] : nullptr;
   a.ds_ld = g.ds_ld[p];
+  a.ds_row0 = qo;
 }
 
 // ============================================================================================
@@ -1490,7 +1516,7 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs ap) {
   BwdArgs a = ap;
   int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
-  if (ap.g.n) bwd_piece(ap, a, bid, nblk);
+  if (ap.g.n) bwd_piece(ap, a, bid, nblk, false);
   using C = DkdvB<D>;
   constexpr int NDB = D / 32;
   // The K/V tiles and the two query-tile buffers are three LDS objects, each
@@ -1831,7 +1857,7 @@ template <int D>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs ap) {
   BwdArgs a = ap;
   int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
-  if (ap.g.n) bwd_piece(ap, a, bid, nblk);
+  if (ap.g.n) bwd_piece(ap, a, bid, nblk, true);
   using C = DqB<D>;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -1991,7 +2017,7 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
   BwdArgs a = ap;
   int bid = (int)blockIdx.x, nblk = (int)gridDim.x;
-  if (ap.g.n) bwd_piece(ap, a, bid, nblk);
+  if (ap.g.n) bwd_piece(ap, a, bid, nblk, true);
   using C = DqsB<D>;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char sbuf0[C::BUF];
@@ -2082,7 +2108,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ds_kernel(BwdArgs ap) {
         const int c = (lane & 15) ^ swz<128>(kr);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (lds_void*)(buf + C::KT + sub * C::ST + (8 * w + 4 * i) * 256), 16,
-            (uint32_t)(ds_offset(jt * DQ_BK + kr, r_first + 128 * sub + 8 * c, a.ds_ld) * 2), 0, 0,
+            (uint32_t)(ds_offset(jt * DQ_BK + kr, a.ds_row0 + r_first + 128 * sub + 8 * c, a.ds_ld) * 2), 0, 0,
             2 /* non-temporal: dS^T is read once */);
       }
   };
@@ -2308,13 +2334,15 @@ hipError_t scratch_device_ptr(void** out) {
 // Launchers
 // ============================================================================================
 
-// Grid of a grouped launch: each piece gets ceil(len / rows) x heads x batch
-// blocks, rounded up to a multiple of 8; fills g.wg_begin.
-static unsigned group_grid(PieceTable& g, int rows, int heads, int batch) {
+// Grid of a grouped launch: each piece gets ceil(n / rows) x heads x batch
+// blocks, rounded up to a multiple of 8, where n is the piece's length, or
+// for the query-side kernels (`qside`) its rows from qoff on; fills g.wg_begin.
+static unsigned group_grid(PieceTable& g, int rows, int heads, int batch, bool qside) {
   int64_t acc = 0;
   for (int p = 0; p < g.n; ++p) {
     g.wg_begin[p] = (int32_t)acc;
-    const int64_t blocks = (int64_t)((g.len[p] + rows - 1) / rows) * heads * batch;
+    const int64_t n = g.len[p] - (qside ? g.qoff[p] : 0);
+    const int64_t blocks = (int64_t)((n + rows - 1) / rows) * heads * batch;
     acc += (blocks + 7) / 8 * 8;
   }
   g.wg_begin[g.n] = (int32_t)acc;
@@ -2323,7 +2351,7 @@ static unsigned group_grid(PieceTable& g, int rows, int heads, int batch) {
 
 hipError_t launch_fwd(const FwdArgs& a0, int head_dim, bool bf16, hipStream_t s) {
   FwdArgs a = a0;
-  const unsigned grid = a.g.n ? group_grid(a.g, FWD_BQ, a.heads, a.batch)
+  const unsigned grid = a.g.n ? group_grid(a.g, FWD_BQ, a.heads, a.batch, true)
                               : (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (a.g.n && !bf16) return hipErrorInvalidValue;  // only the bf16 kernel takes a piece table
@@ -2347,7 +2375,7 @@ hipError_t launch_bwd_fused_f32(const BwdArgs& a, int head_dim, hipStream_t s) {
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a0, int head_dim, hipStream_t s) {
   BwdArgs a = a0;
-  const unsigned grid = a.g.n ? group_grid(a.g, BWD_BK, a.heads, a.batch)
+  const unsigned grid = a.g.n ? group_grid(a.g, BWD_BK, a.heads, a.batch, false)
                               : (unsigned)((int64_t)a.n_ktiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(512), 0, s, a);
@@ -2357,7 +2385,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a0, int head_dim, hipStream_t s) {
 
 hipError_t launch_bwd_dq_ds(const BwdArgs& a0, int head_dim, hipStream_t s) {
   BwdArgs a = a0;
-  const unsigned grid = a.g.n ? group_grid(a.g, DQS_ROWS, a.heads, a.batch)
+  const unsigned grid = a.g.n ? group_grid(a.g, DQS_ROWS, a.heads, a.batch, true)
                               : (unsigned)((int64_t)((a.lq + DQS_ROWS - 1) / DQS_ROWS) * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_ds_kernel<128>), dim3(grid), dim3(512), 0, s, a);
@@ -2367,7 +2395,7 @@ hipError_t launch_bwd_dq_ds(const BwdArgs& a0, int head_dim, hipStream_t s) {
 
 hipError_t launch_bwd_dq(const BwdArgs& a0, int head_dim, hipStream_t s) {
   BwdArgs a = a0;
-  const unsigned grid = a.g.n ? group_grid(a.g, FWD_BQ, a.heads, a.batch)
+  const unsigned grid = a.g.n ? group_grid(a.g, FWD_BQ, a.heads, a.batch, true)
                               : (unsigned)((int64_t)a.n_qtiles * a.heads * a.batch);
   if (grid == 0) return hipSuccess;
   if (head_dim == 128) hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(NT), 0, s, a);
