@@ -1343,9 +1343,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel_bf16(FwdArgs ap) {
     // Tile jt (even offset from jt0: K of jt + 1 in k_buf1, V of jt in v_buf0;
     // odd: the other two) while V of jt + 1 and K of jt + 2 are fetched.
     auto step = [&](int jt, f32x16* cur, f32x16* nxt, const char* sKn, const char* sV, char* dV, char* dK) {
-      // recomputed per tile (a few VALU) rather than held in registers
-      uint32_t c16 = cx16, lks = lk_st, lvs = lv_st;
-      asm volatile("" : "+v"(c16), "+v"(lks), "+v"(lvs));
+      // The copies' per-lane offsets do not change over the loop: held in
+      // registers (8), they cost no VALU issue slots per tile, which the
+      // exponentials and the MFMAs compete for.
+      const uint32_t c16 = cx16, lks = lk_st, lvs = lv_st;
       // Past the end the last tile is fetched again into the free buffer, so
       // that the copies stay in the block of MFMAs; there they are spread one
       // per MFMA (all of a workgroup's copies at once queue up in the
