@@ -39,8 +39,8 @@ def _sample_rows(L, seed, extra=()):
 def _setup(layout, S, N, seed, cu=None):
     import torch
     q, k, v, do = synth.qkv(S, H, D, torch.bfloat16, seed=seed, device=dev(), with_dout=True)
-    kr, idx = ring_from_global(k, layout, N)
-    vr, _ = ring_from_global(v, layout, N)
+    kr, idx = ring_from_global(k, layout, N, cu)
+    vr, _ = ring_from_global(v, layout, N, cu)
     # host float64 copies of the sampled heads only
     hsel = torch.tensor(HEADS, device=dev())
     k64 = f64(k.index_select(2, hsel))
@@ -250,3 +250,43 @@ def test_full_size_varlen_all_slices():
     # all slices together: the complete gradients, still satisfying the identities
     _check_invariants(dk_ring, dv_ring, do.index_select(1, torch.cat(idx)), torch.ones(S, device=dev(),
                       dtype=torch.float64), "varlen all slices")
+
+
+@pytest.mark.parametrize("layout", ["zigzag_varlen", "stripe_varlen"])
+def test_full_size_per_sequence(layout):
+    """The benchmark's per-sequence share: the 13 packed sequences of the varlen
+    workload (131072 tokens), every sequence a ring of 8 of its own, rank 0.
+    Sampled rows include, for every sequence, its first and last local rows, the
+    boundary between its two zigzag chunks and the row from which the forward
+    and dQ launches start after step 0 (a multiple of 16 at or below the second
+    chunk); out, lse and dQ against the oracle, dK/dV through the identities."""
+    import torch
+    ra = _ra()
+    S, N, rank = 131072, 8, 0
+    unit = 2 * N if layout == "zigzag_varlen" else N
+    lengths = synth.round_lengths(synth.loguniform_lengths(S, 1024, 32768, seed=0), unit)
+    cu = synth.cu_seqlens(lengths)
+    log(f"full-size {layout} {len(lengths)} sequences rank {rank}")
+    q, do, kr, vr, idx, k64, v64, hsel = _setup(layout, S, N, seed=0, cu=cu)
+    ql = q.index_select(1, idx[rank]).contiguous()
+    dol = do.index_select(1, idx[rank]).contiguous()
+    out, lse, _ = ra.ring_fwd(layout, N, rank, ql, kr, vr, causal=True, cu_seqlens=cu)
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
+    dq, _, _ = ra.ring_bwd(layout, N, rank, ql, kr, vr, out, lse, dol, causal=True, cu_seqlens=cu,
+                           dk_ring=dk_ring, dv_ring=dv_ring)
+    torch.cuda.synchronize()
+    pos = oracle.layout_positions(layout, S, N, rank, cu)
+    assert np.array_equal(pos, idx[rank].cpu().numpy())
+    L = S // N
+    extra, off = [], 0
+    for n in lengths:
+        loc = n // N                       # this rank's rows of the sequence
+        half = loc // 2                    # zigzag: its first chunk
+        extra += [off, off + 1, off + loc - 1, off + half - 1, off + half, off + half + 1, off + half // 16 * 16]
+        off += loc
+    rows = _sample_rows(L, seed=3, extra=tuple(extra))
+    ro, rl = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, cu, f"{layout} r{rank}")
+    _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, cu, f"{layout} r{rank}")
+    _check_invariants(dk_ring, dv_ring, dol, torch.ones(L, device=dev(), dtype=torch.float64),
+                      f"{layout} r{rank}")
