@@ -290,3 +290,36 @@ def test_full_size_per_sequence(layout):
     _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, cu, f"{layout} r{rank}")
     _check_invariants(dk_ring, dv_ring, dol, torch.ones(L, device=dev(), dtype=torch.float64),
                       f"{layout} r{rank}")
+
+
+def test_full_size_varlen_gathered():
+    """The same packed varlen stream through the gathered-K/V share, as the
+    benchmark runs it: every rank's slice against the whole K/V in one block
+    step (the visible key range only), sampled rows of out, lse and dQ against
+    the oracle, and dK/dV summed over all slices through the identities."""
+    import torch
+    ra = _ra()
+    layout, S, N = "contiguous", 131072, 8
+    lengths = synth.loguniform_lengths(S, 1024, 32768, seed=0)
+    cu = synth.cu_seqlens(lengths)
+    log(f"full-size varlen gathered {len(lengths)} sequences")
+    q, do, _, _, idx, k64, v64, hsel = _setup(layout, S, N, seed=0, cu=cu)
+    k, v = synth.qkv(S, H, D, torch.bfloat16, seed=0, device=dev())[1:3]
+    L = S // N
+    dk_all = torch.zeros((1, S, H, D), device=dev(), dtype=torch.float32)
+    dv_all = torch.zeros_like(dk_all)
+    for r in range(N):
+        ql = q.index_select(1, idx[r]).contiguous()
+        dol = do.index_select(1, idx[r]).contiguous()
+        out, lse, _ = ra.gathered_fwd(layout, N, r, ql, k, v, causal=True, cu_seqlens=cu)
+        dq, _, _ = ra.gathered_bwd(layout, N, r, ql, k, v, out, lse, dol, causal=True, cu_seqlens=cu,
+                                   dk_all=dk_all, dv_all=dv_all)
+        torch.cuda.synchronize()
+        pos = oracle.layout_positions(layout, S, N, r)
+        starts = [int(c) - r * L for c in cu[:-1] if r * L <= c < (r + 1) * L]
+        rows = _sample_rows(L, seed=30 + r, extra=tuple(starts) + tuple(s + 1 for s in starts))
+        ro, rl = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, cu, f"gathered r{r}")
+        if r in (0, 5):
+            _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, cu, f"gathered r{r}")
+    _check_invariants(dk_all[None], dv_all[None], do, torch.ones(S, device=dev(), dtype=torch.float64),
+                      "gathered all slices")
