@@ -122,7 +122,9 @@ def _check_tail_dkdv(q, do, dk_ring, dv_ring, pos, idx, k64, v64, hsel, what, ta
 
 
 @pytest.mark.parametrize("layout,S,rank", [("zigzag", 131072, 0), ("zigzag", 131072, 5),
-                                           ("stripe", 262144, 0)])
+                                           ("stripe", 262144, 0),
+                                           # one million tokens: the backward's dS^T in 32 key chunks per step
+                                           ("zigzag", 1048576, 0)])
 def test_full_size_fwd_bwd(layout, S, rank):
     import torch
     ra = _ra()
