@@ -200,21 +200,35 @@ def test_full_size_full_heads(layout, S, rank, heads):
 
 
 def test_full_size_contiguous_all_ranks():
-    """Contiguous causal ring over 32768 tokens: every rank's forward share."""
+    """Contiguous causal ring over 32768 tokens: every rank's share, forward and
+    backward (ranks 0 to 7 run 1 to 8 ring steps)."""
     import torch
     ra = _ra()
     layout, S, N = "contiguous", 32768, 8
     log("full-size contiguous S=32768 all ranks")
     q, do, kr, vr, idx, k64, v64, hsel = _setup(layout, S, N, seed=0)
     L = S // N
+    dk_ring = torch.zeros(kr.shape, device=dev(), dtype=torch.float32)
+    dv_ring = torch.zeros(vr.shape, device=dev(), dtype=torch.float32)
     for r in range(N):
         ql = q.index_select(1, idx[r]).contiguous()
+        dol = do.index_select(1, idx[r]).contiguous()
         out, lse, lowp = ra.ring_fwd(layout, N, r, ql, kr, vr, causal=True, want_lowp=True)
+        dk_r = torch.zeros_like(dk_ring)
+        dv_r = torch.zeros_like(dv_ring)
+        dq, _, _ = ra.ring_bwd(layout, N, r, ql, kr, vr, out, lse, dol, causal=True, dk_ring=dk_r, dv_ring=dv_r)
         torch.cuda.synchronize()
         pos = oracle.layout_positions(layout, S, N, r)
         rows = _sample_rows(L, seed=10 + r)
-        ro, _ = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, None, f"contiguous r{r}")
+        ro, rl = _check_fwd_rows(q, out, lse, pos, rows, k64, v64, hsel, None, f"contiguous r{r}")
         check_out(f64(lowp.index_select(2, hsel))[:, rows], ro, True, what=f"contiguous r{r} out_lowp")
+        if r in (0, N - 1):
+            _check_dq_rows(q, do, dq, ro, rl, pos, rows, k64, v64, hsel, None, f"contiguous r{r}")
+        _check_invariants(dk_r, dv_r, dol, torch.ones(L, device=dev(), dtype=torch.float64), f"contiguous r{r}")
+        dk_ring += dk_r
+        dv_ring += dv_r
+    _check_invariants(dk_ring, dv_ring, do.index_select(1, torch.cat(idx)), torch.ones(S, device=dev(),
+                      dtype=torch.float64), "contiguous all ranks")
 
 
 def test_full_size_varlen_all_slices():
